@@ -1,0 +1,211 @@
+"""Benchmark: tree-verification attention at the Llama-3.1-8B layer shape.
+
+One step = one hta_verify_attn call (tree kernel + split-KV prefix kernel +
+merge) over one batch of synthetic inputs: 32 query / 8 KV heads, head_dim
+128, a 32768-token bf16 KV prefix and a 64-node draft tree. Inputs are
+resident in HBM before the timed region; the KV cache is rotated over
+enough replicas (>= 512 MB) that the 256 MB Infinity Cache cannot hold the
+next step's KV, so every step streams its KV from HBM.
+
+Prints one JSON line. ``value`` is the layer's achieved HBM bandwidth on
+its algorithmic bytes (valid KV read once + q, tree K/V, out, lse, tree
+shape); the per-layer latency, verified tokens/s, the split-KV kernel's
+roofline (timed alone over the same rotation) and the fp64 CPU oracle's
+throughput on a bounded sample of the same workload are reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("verify-attn layer µs + achieved HBM GB/s (% peak), 8B GQA shape, 32k ctx, "
+          "64-node tree")
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_KEY = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_mfma_llama8b_32k_traffic.txt")
+PREFIX_SRC = os.path.join(ROOT, "speculative_decoding_verification_hybrid_amd", "csrc", "prefix_mfma.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replica-bytes", type=float, default=512e6,
+                    help="total KV bytes to rotate over (cold-cache protocol)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w):
+    s = 2 if w.dtype == "bf16" else 4
+    kv = 2 * w.Hkv * w.D * int(w.prefix_len.sum()) * s
+    tree_kv = 2 * w.B * w.Hkv * w.T * w.D * s
+    q_out = 2 * w.B * w.Hq * w.T * w.D * s
+    lse = w.B * w.Hq * w.T * 4
+    meta = w.B * w.T * 4 + w.B * 4
+    return kv, kv + tree_kv + q_out + lse + meta
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the split-KV kernel from a committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for ln in open(TRAFFIC_FILE):
+        if "=" in ln and not ln.startswith("#"):
+            k, v = ln.split("=", 1)
+            fields[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(PREFIX_SRC, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, min_seconds):
+    """The fp64 oracle on the same workload, repeated until min_seconds of wall time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify_attn(w)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    _, total = algorithmic_bytes(w)
+    gbs = total * reps / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the whole workload (all {w.Hq} query heads, {w.T} tree nodes, "
+                      f"{int(w.prefix_len[0])}-token prefix) {reps} times, {dt:.2f} s wall, "
+                      f"{dt / reps * 1e3:.1f} ms per layer"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the split-KV path "
+              "shards across GPUs by KV head or context, which this build does not launch.")
+        sys.exit(2)
+
+    import torch
+    from speculative_decoding_verification_hybrid_amd import hta
+    from workloads import CONFIGS, make_workload
+
+    c = CONFIGS[WORKLOAD_KEY]
+    w = make_workload(WORKLOAD_KEY)
+    kv_bytes, total_bytes = algorithmic_bytes(w)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, kt, vt = dev(w.q), dev(w.k_tree), dev(w.v_tree)
+    parent = torch.from_numpy(w.parent).cuda()
+    plen = torch.from_numpy(w.prefix_len).cuda()
+    kc0, vc0 = dev(w.k_cache), dev(w.v_cache)
+    R = max(1, int(np.ceil(args.replica_bytes / kv_bytes)))
+    kcs = [kc0] + [kc0.clone() for _ in range(R - 1)]
+    vcs = [vc0] + [vc0.clone() for _ in range(R - 1)]
+    out = torch.empty(w.B, w.Hq, w.T, w.D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device="cuda")
+    cfg = hta.make_config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, tree_nodes=w.T,
+                          kv_capacity=w.Lcap, dtype="bf16", softmax_scale=w.scale)
+    h = hta.hta_create(cfg)
+    plan = hta.hta_get_plan(h)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        hta.hta_verify_attn(h, q, kcs[i % R], vcs[i % R], kt, vt, parent, plen, out, lse, stream)
+
+    def prefix_only(i):
+        hta.hta_prefix_partials(h, q, kcs[i % R], vcs[i % R], plen, stream)
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            fn(warmup + i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+        total = ev[0].elapsed_time(ev[steps])
+        return total / steps, per
+
+    # whole layer
+    ms, per = timed(step, args.steps, args.warmup)
+    status = hta.hta_get_status(h)
+    ok = bool(torch.isfinite(out.float()).all().item()) and status == 0
+    # the split-KV prefix kernel alone, same rotation
+    pms, pper = timed(prefix_only, args.steps, args.warmup)
+    hta.hta_destroy(h)
+
+    layer_us = ms * 1e3
+    value = total_bytes / (ms * 1e-3) / 1e9
+    prefix_gbs = kv_bytes / (pms * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "prefix_len": int(w.prefix_len[0]), "tree_nodes": w.T,
+                   "kv_replicas": R},
+        "layer_us": round(layer_us, 3),
+        "layer_us_p10_p50_p90": [round(float(np.percentile(per, p)) * 1e3, 3) for p in (10, 50, 90)],
+        "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "tokens_per_s_verified": round(w.B * w.T / (ms * 1e-3), 1),
+        "outputs_finite_and_status_ok": ok,
+        "plan": {k: plan[k] for k in ("path", "num_workgroups", "waves_per_workgroup",
+                                      "qblocks_per_wave", "row_groups", "compute_units")},
+        "roofline": {
+            "kernel": "prefix_mfma_kernel (split-KV prefix, hta_prefix_partials)",
+            "bound": "hbm",
+            "achieved": round(prefix_gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(prefix_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(pms * 1e3, 3),
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

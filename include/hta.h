@@ -1,0 +1,201 @@
+/*
+ * hta.h -- tree-verification attention (Hybrid Tree Attention) for MI355X (gfx950).
+ *
+ * What the library computes. A target model verifies a draft tree of T
+ * speculative tokens in one pass. In each attention layer every tree token
+ * attends to (a) the whole cached KV prefix of its sequence, which needs no
+ * mask, and (b) the tree tokens on its own root path (itself and its
+ * ancestors), which needs the tree mask. The two parts are computed apart
+ * and combined exactly with the log-sum-exp trick.
+ *   - LongSpec summary pages, section "Fast Tree Attention" (Hybrid Tree
+ *     Attention: cached part without a mask, speculative part with a mask,
+ *     aggregation by log-sum-exp that keeps the result exact).
+ *   - LogitSpec summary page, section "draft tree construction and
+ *     verification" (the tree mask lets the target verify every branch in
+ *     parallel).
+ *
+ * Conventions used by every entry point (readings of points the pages leave
+ * open):
+ *   B batch, Hq query heads, Hkv KV heads (Hq % Hkv == 0, G = Hq / Hkv),
+ *   D head_dim (64 or 128), T tree nodes (1..64), Lcap KV capacity.
+ *   Query head h reads KV head h / G.
+ *   Tensors are dense, row-major, contiguous device memory:
+ *     q        [B, Hq,  T,    D]   dtype
+ *     k_cache  [B, Hkv, Lcap, D]   dtype   (positions >= prefix_len[b] are never read)
+ *     v_cache  [B, Hkv, Lcap, D]   dtype   (same)
+ *     k_tree   [B, Hkv, T,    D]   dtype   (post-RoPE keys of the tree tokens)
+ *     v_tree   [B, Hkv, T,    D]   dtype
+ *     parent   [B, T] int32: parent[b][0] == -1 and -1 <= parent[b][i] < i
+ *              (nodes in topological order; an extra -1 starts another root)
+ *     prefix_len [B] int32: 0 <= prefix_len[b] <= Lcap
+ *     out      [B, Hq, T, D]   dtype
+ *     lse      [B, Hq, T] float32: natural log of sum(exp(scale * q.k)) over
+ *              the visible keys (the scaled-score convention).
+ *   dtype is HTA_BF16 (bfloat16 storage, float32 arithmetic) or HTA_F32.
+ *   The softmax scale defaults to 1/sqrt(D).
+ *
+ * Float tensors (q, k/v cache, k/v tree, out and the float32 partials) must
+ * start on a 16-byte boundary; a misaligned pointer is HTA_ERR_INVALID_ARG.
+ *
+ * Ownership: the caller allocates and owns every tensor argument. A handle
+ * owns only its device workspace (partial results and status words), sized
+ * at hta_create. Every pointer argument named as a tensor above is a device
+ * pointer; the only host pointers are the handle, config, plan and status
+ * out-parameters.
+ *
+ * Streams: `stream` is a hipStream_t (NULL means the null stream). Calls are
+ * asynchronous: they validate on the host, enqueue kernels and return. The
+ * workspace is shared by all calls on one handle, so at most one call per
+ * handle may be in flight (use one handle per concurrent stream).
+ *
+ * Errors: functions return HTA_OK (0) or a negative HTA_ERR_* code; nothing
+ * throws and the library never prints. Host-side checks (null pointers,
+ * unsupported shapes) fail before any kernel is enqueued. Checks that need
+ * device data (a parent array that breaks the rule above, a prefix_len
+ * outside [0, Lcap]) cannot fail the call; instead the affected sequence's
+ * outputs are filled with NaN and a sticky bit is set in the handle's device
+ * status word, read (and cleared) by hta_get_status. Enqueue failures map to
+ * HTA_ERR_HIP.
+ */
+#ifndef HTA_H_
+#define HTA_H_
+
+#include <stdint.h>
+
+#ifndef HTA_API
+#define HTA_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hta_handle_s* hta_handle_t;
+
+enum hta_status_code {
+  HTA_OK = 0,
+  HTA_ERR_INVALID_ARG = -1, /* null pointer, bad size or an impossible config */
+  HTA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64,128}, T > 64, ... */
+  HTA_ERR_NO_MEMORY = -3,   /* workspace allocation failed */
+  HTA_ERR_HIP = -4,         /* a HIP runtime call or kernel enqueue failed */
+  HTA_ERR_BAD_TREE = -5,    /* reported through hta_get_status only */
+  HTA_ERR_BAD_PREFIX = -6,  /* reported through hta_get_status only */
+  HTA_ERR_NO_DEVICE = -7    /* no usable GPU */
+};
+
+enum hta_dtype { HTA_F32 = 0, HTA_BF16 = 1 };
+
+/* Bits of the device status word (see hta_get_status). */
+enum hta_device_status { HTA_STATUS_BAD_TREE = 1, HTA_STATUS_BAD_PREFIX = 2 };
+
+/* Prefix-kernel implementation (see hta_plan_t.path). */
+enum hta_path { HTA_PATH_AUTO = 0, HTA_PATH_MFMA = 1, HTA_PATH_VALU = 2 };
+
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t n_q_heads;      /* Hq >= 1 */
+  int32_t n_kv_heads;     /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;       /* D: 64 or 128 */
+  int32_t tree_nodes;     /* T: 1..64 */
+  int32_t kv_capacity;    /* Lcap >= 1 */
+  int32_t dtype;          /* enum hta_dtype */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(D) */
+  int32_t num_workgroups; /* prefix-kernel workgroups; 0 = sized from the device */
+  int32_t force_path;     /* enum hta_path; AUTO picks MFMA for bf16 with G*T >= 16 */
+} hta_config_t;
+
+typedef struct {
+  int32_t path;                /* HTA_PATH_MFMA or HTA_PATH_VALU */
+  int32_t num_workgroups;      /* workgroups per row group of the prefix kernel */
+  int32_t row_groups;          /* prefix-kernel grid.y: row groups per KV head */
+  int32_t rows_per_group;      /* query rows (of G*T per KV head) per row group */
+  int32_t waves_per_workgroup;
+  int32_t qblocks_per_wave;    /* 32-row MFMA blocks per wave (MFMA path) */
+  int32_t tile_tokens;         /* prefix tokens per pipeline stage */
+  int32_t max_slots;           /* partial-result slots in the workspace */
+  int64_t workspace_bytes;
+  int32_t device;              /* HIP device the handle was created on */
+  int32_t compute_units;
+} hta_plan_t;
+
+/* Host-only validation of a config; makes no HIP call. Returns HTA_OK,
+ * HTA_ERR_INVALID_ARG or HTA_ERR_UNSUPPORTED. */
+HTA_API int hta_validate_config(const hta_config_t* cfg);
+
+/* Validates cfg, plans the launch for the current HIP device and allocates
+ * the workspace. On success *out holds a new handle; on failure *out is NULL. */
+HTA_API int hta_create(hta_handle_t* out, const hta_config_t* cfg);
+
+/* Frees the workspace and the handle (synchronises the device first).
+ * NULL is accepted and ignored. */
+HTA_API int hta_destroy(hta_handle_t h);
+
+/* Copies the launch plan chosen at hta_create. Host only. */
+HTA_API int hta_get_plan(hta_handle_t h, hta_plan_t* plan);
+
+/* Full verification attention: prefix part (split-KV over all compute units,
+ * no mask) + tree part (ancestor mask) + exact log-sum-exp merge.
+ * Layouts and rules as in the header comment. out has the handle's dtype;
+ * lse is float32 natural log. LongSpec, "Fast Tree Attention". */
+HTA_API int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                    const void* k_tree, const void* v_tree, const int32_t* parent,
+                    const int32_t* prefix_len, void* out, float* lse, void* stream);
+
+/* The tree mask alone: mask_out[b][i] (uint64, device) has bit j set iff
+ * tree node j is node i or one of its ancestors. A sequence whose parent
+ * array breaks the rule gets all-zero words and sets HTA_STATUS_BAD_TREE.
+ * LogitSpec, "draft tree construction and verification". */
+HTA_API int hta_tree_mask(hta_handle_t h, const int32_t* parent, uint64_t* mask_out, void* stream);
+
+/* The speculative (tree) part alone: attention of every tree token over the
+ * tree tokens it may see. o_tree [B,Hq,T,D] float32 (normalised), lse_tree
+ * [B,Hq,T] float32 natural log. Bad trees give NaN rows + status bit.
+ * LongSpec, "Fast Tree Attention" (the masked speculative part). */
+HTA_API int hta_tree_attn(hta_handle_t h, const void* q, const void* k_tree, const void* v_tree,
+                  const int32_t* parent, float* o_tree, float* lse_tree, void* stream);
+
+/* The cached (prefix) part alone: attention of every tree token over the
+ * first prefix_len[b] cache positions, unmasked, computed split-KV and
+ * merged. o_prefix [B,Hq,T,D] float32 (normalised), lse_prefix [B,Hq,T]
+ * float32 natural log; a sequence with prefix_len 0 gives o = 0 and
+ * lse = -inf. A prefix_len outside [0, Lcap] gives NaN rows + status bit.
+ * LongSpec, "Fast Tree Attention" (the cached part, no mask needed). */
+HTA_API int hta_prefix_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* prefix_len, float* o_prefix, float* lse_prefix, void* stream);
+
+/* The split-KV prefix kernel alone (the first half of hta_prefix_attn): leaves
+ * one normalised partial per (workgroup, sequence/KV-head piece) in the
+ * handle's workspace, to be combined by hta_merge_prefix. Used to time and
+ * test the kernel that streams the KV cache. LongSpec, "Fast Tree Attention"
+ * (the cached part, no mask needed). */
+HTA_API int hta_prefix_partials(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* prefix_len, void* stream);
+
+/* Merges the partials of the last hta_prefix_partials call on this handle
+ * (prefix_len must hold the same values) into o_prefix [B,Hq,T,D] float32
+ * and lse_prefix [B,Hq,T] float32 natural log, exactly as hta_prefix_attn. */
+HTA_API int hta_merge_prefix(hta_handle_t h, const int32_t* prefix_len, float* o_prefix,
+                             float* lse_prefix, void* stream);
+
+/* Exact log-sum-exp merge of n_parts normalised partial attentions over
+ * disjoint key sets: o_parts [n_parts][B,Hq,T,D] float32, lse_parts
+ * [n_parts][B,Hq,T] float32 natural log (-inf marks an empty part). Writes
+ * out [B,Hq,T,D] float32 and lse [B,Hq,T] float32:
+ *   lse = ln(sum_k exp(lse_k)),  out = sum_k exp(lse_k - lse) * o_k.
+ * Rows where every part is empty get out = 0, lse = -inf. 1 <= n_parts <= 4096.
+ * LongSpec, "Fast Tree Attention" (aggregation with the log-sum-exp trick). */
+HTA_API int hta_lse_merge(hta_handle_t h, int32_t n_parts, const float* o_parts, const float* lse_parts,
+                  float* out, float* lse, void* stream);
+
+/* Synchronises `stream`, returns in *device_status the OR of the status
+ * bits raised since the last call (HTA_STATUS_*), and clears them. */
+HTA_API int hta_get_status(hta_handle_t h, void* stream, int32_t* device_status);
+
+/* Static English text for a return code. Never NULL. */
+HTA_API const char* hta_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HTA_H_ */

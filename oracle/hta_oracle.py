@@ -179,6 +179,8 @@ def lse_merge(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):
     with np.errstate(divide="ignore"):
         lse = np.where(empty, -np.inf, mxs + np.log(np.where(empty, 1.0, tot)))
     coef = np.where(empty[None], 0.0, wts / np.where(empty, 1.0, tot)[None])
+    # an empty part (lse = -inf) adds nothing, whatever its o holds
+    O = np.where(np.isneginf(L)[..., None], 0.0, O)
     out = (coef[..., None] * O).sum(axis=0)
     return out, lse
 

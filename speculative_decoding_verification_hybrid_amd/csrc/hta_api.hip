@@ -1,0 +1,305 @@
+// C ABI of libhta: handle, launch planning, workspace and the entry points
+// declared in include/hta.h.
+#include <math.h>
+#include <new>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "common.h"
+#include "hta.h"
+#include "hta_internal.h"
+
+struct hta_handle_s {
+  hta_config_t cfg;
+  hta::Dims dims;
+  hta::PrefixLaunch pl;
+  hta_plan_t plan;
+  void* ws;
+  hta::Slots slots;
+  float* o_tree;     // [B,Hq,T,D] tree partial (normalised)
+  float* lse2_tree;  // [B,Hq,T] log2 domain
+  int* err_b;        // [B] bad-tree flags of the last call
+  int* status;       // sticky HTA_STATUS_* bits
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_hip(hipError_t e) { return e == hipSuccess ? HTA_OK : HTA_ERR_HIP; }
+
+// Tensor arguments are read with 16-byte vector loads.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+template <typename... P>
+bool all_aligned(const P*... p) {
+  return (aligned16(p) && ...);
+}
+
+int validate(const hta_config_t* c) {
+  if (!c) return HTA_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->tree_nodes < 1 || c->kv_capacity < 1)
+    return HTA_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads != 0) return HTA_ERR_INVALID_ARG;
+  if (c->dtype != HTA_F32 && c->dtype != HTA_BF16) return HTA_ERR_INVALID_ARG;
+  if (c->num_workgroups < 0) return HTA_ERR_INVALID_ARG;
+  if (c->force_path < HTA_PATH_AUTO || c->force_path > HTA_PATH_VALU) return HTA_ERR_INVALID_ARG;
+  if (!(c->softmax_scale == c->softmax_scale)) return HTA_ERR_INVALID_ARG;  // NaN
+  if (c->head_dim != 64 && c->head_dim != 128) return HTA_ERR_UNSUPPORTED;
+  if (c->tree_nodes > 64) return HTA_ERR_UNSUPPORTED;
+  if (c->force_path == HTA_PATH_MFMA && c->dtype != HTA_BF16) return HTA_ERR_UNSUPPORTED;
+  // Index arithmetic limits: rows and per-sequence KV spans stay within int32.
+  const int64_t rows = (int64_t)c->batch * c->n_q_heads * c->tree_nodes;
+  if (rows * c->head_dim > INT32_MAX) return HTA_ERR_UNSUPPORTED;
+  if ((int64_t)c->kv_capacity * c->head_dim > INT32_MAX) return HTA_ERR_UNSUPPORTED;
+  if ((int64_t)c->batch * c->n_kv_heads > (1 << 20)) return HTA_ERR_UNSUPPORTED;
+  return HTA_OK;
+}
+
+// Prefix-kernel shape: MFMA path blocks of 32 query rows, at most 8 per
+// workgroup (two per wave on 4 waves, or one per wave on up to 8 waves);
+// VALU path 16 rows per workgroup.
+void plan_rows(const hta::Dims& d, int path, hta::PrefixLaunch* pl) {
+  pl->path = path;
+  if (path == HTA_PATH_MFMA) {
+    const int nqb = (d.M + 31) / 32;
+    const int rg = (nqb + 7) / 8;
+    const int per = (nqb + rg - 1) / rg;
+    pl->row_groups = rg;
+    pl->rows_per_group = per * 32;
+    if (per == 8) {
+      pl->waves = 4;
+      pl->qb = 2;
+    } else {
+      pl->waves = per;
+      pl->qb = 1;
+    }
+  } else {
+    pl->row_groups = (d.M + 15) / 16;
+    pl->rows_per_group = 16;
+    pl->waves = 4;
+    pl->qb = 0;
+  }
+}
+
+#define HTA_TRY(expr)             \
+  do {                            \
+    int rc_ = (expr);             \
+    if (rc_ != HTA_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int hta_validate_config(const hta_config_t* cfg) { return validate(cfg); }
+
+const char* hta_status_string(int status) {
+  switch (status) {
+    case HTA_OK: return "ok";
+    case HTA_ERR_INVALID_ARG: return "invalid argument";
+    case HTA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case HTA_ERR_NO_MEMORY: return "workspace allocation failed";
+    case HTA_ERR_HIP: return "HIP runtime error";
+    case HTA_ERR_BAD_TREE: return "parent array breaks -1 <= parent[i] < i";
+    case HTA_ERR_BAD_PREFIX: return "prefix_len outside [0, kv_capacity]";
+    case HTA_ERR_NO_DEVICE: return "no usable GPU";
+    default: return "unknown status";
+  }
+}
+
+int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
+  if (!out) return HTA_ERR_INVALID_ARG;
+  *out = nullptr;
+  HTA_TRY(validate(cfg));
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HTA_ERR_NO_DEVICE;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return HTA_ERR_NO_DEVICE;
+
+  hta_handle_s* h = new (std::nothrow) hta_handle_s();
+  if (!h) return HTA_ERR_NO_MEMORY;
+  h->cfg = *cfg;
+  hta::Dims& d = h->dims;
+  d.B = cfg->batch;
+  d.Hq = cfg->n_q_heads;
+  d.Hkv = cfg->n_kv_heads;
+  d.G = d.Hq / d.Hkv;
+  d.T = cfg->tree_nodes;
+  d.D = cfg->head_dim;
+  d.Lcap = cfg->kv_capacity;
+  d.M = d.G * d.T;
+  d.bf16 = cfg->dtype == HTA_BF16;
+  const float scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)d.D);
+  d.scale_log2 = scale * hta::kLog2e;
+
+  int path = cfg->force_path;
+  if (path == HTA_PATH_AUTO) path = (d.bf16 && d.M >= 16) ? HTA_PATH_MFMA : HTA_PATH_VALU;
+  plan_rows(d, path, &h->pl);
+  if (path == HTA_PATH_MFMA && !hta::prefix_mfma_supported(d.D, h->pl.waves, h->pl.qb)) {
+    delete h;
+    return HTA_ERR_UNSUPPORTED;
+  }
+  const int occ = path == HTA_PATH_MFMA ? hta::prefix_mfma_occupancy(d.D, h->pl.waves, h->pl.qb)
+                                        : hta::prefix_valu_occupancy(d.D, d.bf16);
+  int64_t nwg = cfg->num_workgroups;
+  if (nwg <= 0) {
+    nwg = (int64_t)cus * (occ > 0 ? occ : 1) / h->pl.row_groups;
+    nwg = nwg < 8 ? 8 : (nwg / 8) * 8;
+    const int64_t max_tiles = (int64_t)d.B * d.Hkv * ((d.Lcap + hta::kTileTokens - 1) / hta::kTileTokens);
+    if (nwg > max_tiles) nwg = max_tiles;
+  }
+  if (nwg > (1 << 20)) nwg = 1 << 20;
+  h->pl.nwg = (int)nwg;
+
+  const int64_t max_slots = nwg + (int64_t)d.B * d.Hkv - 1;
+  const size_t rows = (size_t)d.B * d.Hq * d.T;
+  size_t off = 0;
+  const size_t off_so = off;
+  off = align256(off + (size_t)max_slots * d.M * d.D * sizeof(float));
+  const size_t off_sl = off;
+  off = align256(off + (size_t)max_slots * d.M * sizeof(float));
+  const size_t off_ot = off;
+  off = align256(off + rows * d.D * sizeof(float));
+  const size_t off_lt = off;
+  off = align256(off + rows * sizeof(float));
+  const size_t off_eb = off;
+  off = align256(off + (size_t)d.B * sizeof(int));
+  const size_t off_st = off;
+  off = align256(off + sizeof(int));
+  if (hipMalloc(&h->ws, off) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return HTA_ERR_NO_MEMORY;
+  }
+  char* base = static_cast<char*>(h->ws);
+  h->slots.o = reinterpret_cast<float*>(base + off_so);
+  h->slots.lse2 = reinterpret_cast<float*>(base + off_sl);
+  h->o_tree = reinterpret_cast<float*>(base + off_ot);
+  h->lse2_tree = reinterpret_cast<float*>(base + off_lt);
+  h->err_b = reinterpret_cast<int*>(base + off_eb);
+  h->status = reinterpret_cast<int*>(base + off_st);
+  if (hipMemset(base + off_eb, 0, off - off_eb) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(h->ws);
+    delete h;
+    return HTA_ERR_HIP;
+  }
+
+  hta_plan_t& p = h->plan;
+  p.path = path;
+  p.num_workgroups = h->pl.nwg;
+  p.row_groups = h->pl.row_groups;
+  p.rows_per_group = h->pl.rows_per_group;
+  p.waves_per_workgroup = h->pl.waves;
+  p.qblocks_per_wave = h->pl.qb;
+  p.tile_tokens = hta::kTileTokens;
+  p.max_slots = (int32_t)max_slots;
+  p.workspace_bytes = (int64_t)off;
+  p.device = dev;
+  p.compute_units = cus;
+  *out = h;
+  return HTA_OK;
+}
+
+int hta_destroy(hta_handle_t h) {
+  if (!h) return HTA_OK;
+  int rc = HTA_OK;
+  int cur = 0;
+  if (hipGetDevice(&cur) == hipSuccess && cur != h->plan.device) (void)hipSetDevice(h->plan.device);
+  if (hipDeviceSynchronize() != hipSuccess) rc = HTA_ERR_HIP;
+  if (hipFree(h->ws) != hipSuccess) rc = HTA_ERR_HIP;
+  if (cur != h->plan.device) (void)hipSetDevice(cur);
+  delete h;
+  return rc;
+}
+
+int hta_get_plan(hta_handle_t h, hta_plan_t* plan) {
+  if (!h || !plan) return HTA_ERR_INVALID_ARG;
+  *plan = h->plan;
+  return HTA_OK;
+}
+
+int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                    const void* k_tree, const void* v_tree, const int32_t* parent,
+                    const int32_t* prefix_len, void* out, float* lse, void* stream) {
+  if (!h || !q || !k_cache || !v_cache || !k_tree || !v_tree || !parent || !prefix_len || !out || !lse)
+    return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(q, k_cache, v_cache, k_tree, v_tree, out)) return HTA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hta::Dims& d = h->dims;
+  HTA_TRY(check_hip(hta::launch_tree_attn(d, q, k_tree, v_tree, parent, h->o_tree, h->lse2_tree, 1.0f,
+                                          h->err_b, h->status, s)));
+  if (h->pl.path == HTA_PATH_MFMA)
+    HTA_TRY(check_hip(hta::launch_prefix_mfma(d, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s)));
+  else
+    HTA_TRY(check_hip(hta::launch_prefix_valu(d, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s)));
+  return check_hip(hta::launch_merge_slots(d, h->pl.nwg, prefix_len, h->slots, h->o_tree, h->lse2_tree,
+                                           h->err_b, out, d.bf16, lse, h->status, s));
+}
+
+int hta_tree_mask(hta_handle_t h, const int32_t* parent, uint64_t* mask_out, void* stream) {
+  if (!h || !parent || !mask_out) return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_tree_mask(h->dims, parent, mask_out, h->status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int hta_tree_attn(hta_handle_t h, const void* q, const void* k_tree, const void* v_tree,
+                  const int32_t* parent, float* o_tree, float* lse_tree, void* stream) {
+  if (!h || !q || !k_tree || !v_tree || !parent || !o_tree || !lse_tree) return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(q, k_tree, v_tree, o_tree)) return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_tree_attn(h->dims, q, k_tree, v_tree, parent, o_tree, lse_tree, hta::kLn2,
+                                         nullptr, h->status, static_cast<hipStream_t>(stream)));
+}
+
+int hta_prefix_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* prefix_len, float* o_prefix, float* lse_prefix, void* stream) {
+  if (!h || !q || !k_cache || !v_cache || !prefix_len || !o_prefix || !lse_prefix)
+    return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(q, k_cache, v_cache, o_prefix)) return HTA_ERR_INVALID_ARG;
+  HTA_TRY(hta_prefix_partials(h, q, k_cache, v_cache, prefix_len, stream));
+  return hta_merge_prefix(h, prefix_len, o_prefix, lse_prefix, stream);
+}
+
+int hta_prefix_partials(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* prefix_len, void* stream) {
+  if (!h || !q || !k_cache || !v_cache || !prefix_len) return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(q, k_cache, v_cache)) return HTA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h->pl.path == HTA_PATH_MFMA)
+    return check_hip(hta::launch_prefix_mfma(h->dims, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s));
+  return check_hip(hta::launch_prefix_valu(h->dims, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s));
+}
+
+int hta_merge_prefix(hta_handle_t h, const int32_t* prefix_len, float* o_prefix, float* lse_prefix,
+                     void* stream) {
+  if (!h || !prefix_len || !o_prefix || !lse_prefix) return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(o_prefix)) return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, prefix_len, h->slots, nullptr, nullptr,
+                                           nullptr, o_prefix, false, lse_prefix, h->status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int hta_lse_merge(hta_handle_t h, int32_t n_parts, const float* o_parts, const float* lse_parts,
+                  float* out, float* lse, void* stream) {
+  if (!h || !o_parts || !lse_parts || !out || !lse) return HTA_ERR_INVALID_ARG;
+  if (n_parts < 1 || n_parts > 4096) return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(o_parts, out)) return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_merge_parts(h->dims, n_parts, o_parts, lse_parts, out, lse,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int hta_get_status(hta_handle_t h, void* stream, int32_t* device_status) {
+  if (!h || !device_status) return HTA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, h->status, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return HTA_ERR_HIP;
+  HTA_TRY(check_hip(hta::launch_clear_status(h->status, s)));
+  if (hipStreamSynchronize(s) != hipSuccess) return HTA_ERR_HIP;
+  *device_status = v;
+  return HTA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal interface between the C ABI (hta_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hta {
+
+constexpr int kTileTokens = 64;  // prefix tokens per pipeline stage (both prefix paths)
+
+struct Dims {
+  int B, Hq, Hkv, G, T, D, Lcap, M;  // M = G*T query rows per KV head
+  bool bf16;
+  float scale_log2;                  // softmax scale * log2(e)
+};
+
+// Partial results of the prefix kernels: slot s holds M rows of D floats
+// (normalised output) and M log2-domain LSE values.
+struct Slots {
+  float* o;
+  float* lse2;
+};
+
+struct PrefixLaunch {
+  int path;           // 1 MFMA, 2 VALU
+  int nwg;            // workgroups per row group
+  int row_groups;     // grid.y
+  int rows_per_group; // multiple of 32 (MFMA) or of 16 (VALU)
+  int waves;          // MFMA: WQ
+  int qb;             // MFMA: q-blocks per wave
+};
+
+// Prefix part, split-KV: writes slots.
+hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const void* q,
+                              const void* k_cache, const void* v_cache, const int* prefix_len,
+                              Slots slots, hipStream_t s);
+hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const void* q,
+                              const void* k_cache, const void* v_cache, const int* prefix_len,
+                              Slots slots, hipStream_t s);
+// Occupancy (workgroups per CU) of the chosen prefix kernel, for sizing nwg.
+int prefix_mfma_occupancy(int D, int waves, int qb);
+int prefix_valu_occupancy(int D, bool bf16);
+bool prefix_mfma_supported(int D, int waves, int qb);
+
+// Tree part. lse_scale converts the log2-domain LSE on store (1 keeps log2,
+// ln 2 gives natural log). err_b (may be null) receives per-sequence bad-tree flags.
+hipError_t launch_tree_attn(const Dims& d, const void* q, const void* k_tree, const void* v_tree,
+                            const int* parent, float* o_tree, float* lse_tree, float lse_scale,
+                            int* err_b, int* status, hipStream_t s);
+hipError_t launch_tree_mask(const Dims& d, const int* parent, uint64_t* mask_out, int* status,
+                            hipStream_t s);
+
+// Merge of the prefix slots (+ optional tree partial) into out (float or bf16)
+// and natural-log lse.
+hipError_t launch_merge_slots(const Dims& d, int nwg, const int* prefix_len, Slots slots,
+                              const float* o_tree, const float* lse2_tree, const int* err_b,
+                              void* out, bool out_bf16, float* lse, int* status, hipStream_t s);
+// Merge of n_parts caller-provided partials (natural-log LSE) into float out.
+hipError_t launch_merge_parts(const Dims& d, int n_parts, const float* o_parts,
+                              const float* lse_parts, float* out, float* lse, hipStream_t s);
+
+hipError_t launch_clear_status(int* status, hipStream_t s);
+
+}  // namespace hta

@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: max-abs error on outputs <= 2e-2 for bf16 inputs (fp32
+accumulation) and <= 1e-5 for fp32 inputs; |d lse| <= 1e-3 * max(1, |lse|).
+Mask bits are compared exactly. Full-size workloads compare every output of
+sampled query heads (all sequences, all tree nodes) with the oracle.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL_OUT, assert_close, config_for, io_dtype, run_verify, say, to_device
+from speculative_decoding_verification_hybrid_amd import hta
+from workloads import make_custom, make_workload, tree_chain, tree_star
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_HEADS = {3: [0, 5, 31], 4: [0, 13, 39], 5: [0, 17, 31]}
+
+
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+def test_named_workload_parity(key):
+    say(f"named workload {key}: generate")
+    w = make_workload(key)
+    say(f"named workload {key}: hta_verify_attn")
+    out, lse, status = run_verify(w)
+    assert status == 0
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ref_out, ref_lse = oracle.verify_attn(w, heads=SAMPLE_HEADS.get(key))
+    eo, el = assert_close(w, out, lse, ref_out, ref_lse)
+    say(f"named workload {key}: out err {eo:.2e}, lse rel err {el:.2e}")
+
+
+# ----------------------------------------------------------------------------
+# mask semantics, bit for bit
+# ----------------------------------------------------------------------------
+
+def _random_trees(rng, B, T):
+    out = []
+    for b in range(B):
+        kind = b % 5
+        if kind == 0:
+            p = tree_chain(T)
+        elif kind == 1:
+            p = tree_star(T)
+        elif kind == 2:  # forest: extra roots
+            p = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, T)], dtype=np.int32)
+        else:
+            p = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, T)], dtype=np.int32)
+        out.append(p)
+    return np.stack(out).astype(np.int32)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 33, 63, 64])
+def test_tree_mask_bits_exact(T):
+    rng = np.random.default_rng(T)
+    B = 40
+    parents = _random_trees(rng, B, T)
+    say(f"hta_tree_mask T={T} B={B}")
+    cfg = hta.make_config(batch=B, n_q_heads=1, n_kv_heads=1, head_dim=64, tree_nodes=T, kv_capacity=1)
+    with hta.hta_create(cfg) as h:
+        mask = torch.empty(B, T, dtype=torch.int64, device="cuda")
+        hta.hta_tree_mask(h, torch.from_numpy(parents).cuda(), mask)
+        assert hta.hta_get_status(h) == 0
+        got = mask.cpu().numpy().view(np.uint64)
+    for b in range(B):
+        assert np.array_equal(got[b], oracle.tree_mask_bits(parents[b])), b
+
+
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f32", 1), ("bf16", 1)])
+def test_one_hot_probe_shows_exact_visibility(dtype, G):
+    """k = 0, v_cache = 0, v_tree[j] = e_j: out[i, j] > 0 exactly when j is visible to i."""
+    T, D, L = 40, 64, 70
+    w = make_custom(B=2, Hq=2 * G, Hkv=2, D=D, Lcap=L, T=T, prefix_len=[L, 5], dtype=dtype, seed=9,
+                    parents=_random_trees(np.random.default_rng(3), 2, T))
+    for name in ("k_cache", "v_cache", "k_tree"):
+        getattr(w, name)[...] = 0
+    onehot = np.zeros((2, 2, T, D), dtype=np.float32)
+    for j in range(T):
+        onehot[:, :, j, j] = 1.0
+    w.v_tree = onehot if dtype == "f32" else (onehot.view(np.uint32) >> 16).astype(np.uint16)
+    say(f"one-hot probe dtype={dtype} G={G}")
+    out, lse, status = run_verify(w)
+    assert status == 0
+    for b in range(2):
+        bits = oracle.tree_mask_bits(w.parent[b])
+        n_prefix = int(w.prefix_len[b])
+        for h in range(2 * G):
+            for i in range(T):
+                vis = np.array([(int(bits[i]) >> j) & 1 for j in range(T)], dtype=bool)
+                assert np.array_equal(out[b, h, i, :T] > 0, vis), (b, h, i)
+                want = 1.0 / (n_prefix + vis.sum())
+                assert np.allclose(out[b, h, i, :T][vis], want, rtol=1e-2)
+                assert np.isclose(lse[b, h, i], np.log(n_prefix + vis.sum()), rtol=1e-3)
+
+
+# ----------------------------------------------------------------------------
+# shapes and edge cases
+# ----------------------------------------------------------------------------
+
+EDGE = {
+    # name: make_custom kwargs (+ optional config kwargs under "cfg")
+    "pure_tree_L0": dict(B=2, Hq=8, Hkv=2, D=128, Lcap=128, T=20, prefix_len=[0, 0]),
+    "single_node": dict(B=1, Hq=8, Hkv=2, D=128, Lcap=300, T=1, prefix_len=[300]),
+    "single_node_L0": dict(B=1, Hq=4, Hkv=4, D=64, Lcap=8, T=1, prefix_len=[0]),
+    "chain_tree": dict(B=1, Hq=8, Hkv=2, D=128, Lcap=333, T=33, prefix_len=[333], parents=[tree_chain(33)]),
+    "star_tree": dict(B=1, Hq=8, Hkv=2, D=128, Lcap=200, T=17, prefix_len=[190], parents=[tree_star(17)]),
+    "forest": dict(B=1, Hq=4, Hkv=1, D=128, Lcap=130, T=12, prefix_len=[129],
+                   parents=[[-1, 0, -1, 2, 1, -1, 5, 6, 0, 3, 9, 4]]),
+    "ragged_tails": dict(B=6, Hq=8, Hkv=2, D=128, Lcap=1000, T=16, prefix_len=[1, 63, 64, 65, 1000, 0]),
+    "poison_tail": dict(B=3, Hq=8, Hkv=2, D=128, Lcap=500, T=16, prefix_len=[77, 500, 1], poison_tail=True),
+    "full_capacity": dict(B=1, Hq=8, Hkv=8, D=128, Lcap=777, T=26, prefix_len=[777]),
+    "d64_mfma": dict(B=2, Hq=16, Hkv=4, D=64, Lcap=900, T=16, prefix_len=[900, 450]),
+    "gqa_odd_rows": dict(B=2, Hq=6, Hkv=2, D=128, Lcap=700, T=7, prefix_len=[700, 321]),
+    "m160_five_waves": dict(B=2, Hq=10, Hkv=2, D=128, Lcap=1100, T=32, prefix_len=[1100, 613]),
+    "m512_two_row_groups": dict(B=1, Hq=16, Hkv=2, D=128, Lcap=640, T=64, prefix_len=[640]),
+    "m224_seven_waves": dict(B=1, Hq=14, Hkv=2, D=128, Lcap=600, T=32, prefix_len=[599]),
+    "bf16_small_rows_valu": dict(B=2, Hq=4, Hkv=4, D=128, Lcap=500, T=8, prefix_len=[500, 77]),
+    "bf16_forced_valu": dict(B=1, Hq=8, Hkv=2, D=128, Lcap=400, T=16, prefix_len=[390],
+                             cfg=dict(force_path=hta.HTA_PATH_VALU)),
+    "f32_ragged": dict(B=3, Hq=4, Hkv=2, D=64, Lcap=300, T=8, prefix_len=[300, 129, 0], dtype="f32"),
+    "f32_d128": dict(B=1, Hq=4, Hkv=1, D=128, Lcap=200, T=13, prefix_len=[190], dtype="f32"),
+    "drift_keys": dict(B=1, Hq=8, Hkv=2, D=128, Lcap=5000, T=32, prefix_len=[5000], drift=True,
+                       tree=("bounded", 8, None)),
+    "scale_override": dict(B=1, Hq=8, Hkv=2, D=128, Lcap=256, T=16, prefix_len=[256], scale=0.3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_case_parity(name):
+    kw = dict(EDGE[name])
+    cfg_kw = kw.pop("cfg", {})
+    kw.setdefault("dtype", "bf16")
+    w = make_custom(seed=zlib.crc32(name.encode()) % 1000, **kw)
+    say(f"edge case {name}: hta_verify_attn")
+    out, lse, status = run_verify(w, **cfg_kw)
+    assert status == 0
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ref_out, ref_lse = oracle.verify_attn(w)
+    eo, el = assert_close(w, out, lse, ref_out, ref_lse)
+    say(f"edge case {name}: out err {eo:.2e}, lse rel err {el:.2e}")
+
+
+@pytest.mark.parametrize("nwg", [1, 3, 7, 13, 64, 1000])
+def test_workgroup_count_does_not_change_results(nwg):
+    """Any split of the prefix tiles over workgroups gives the same answer."""
+    w = make_custom(B=4, Hq=8, Hkv=2, D=128, Lcap=1500, T=24, prefix_len=[1500, 64, 999, 1], seed=nwg)
+    say(f"num_workgroups={nwg}")
+    out, lse, status = run_verify(w, num_workgroups=nwg)
+    assert status == 0
+    ref_out, ref_lse = oracle.verify_attn(w)
+    assert_close(w, out, lse, ref_out, ref_lse)
+
+
+def test_runs_are_bitwise_deterministic():
+    w = make_custom(B=2, Hq=32, Hkv=8, D=128, Lcap=4096, T=64, prefix_len=[4096, 3001], seed=5)
+    dev = to_device(w)
+    say("determinism: two identical calls")
+    with hta.hta_create(config_for(w)) as h:
+        a = run_verify(w, dev=dev, handle=h)
+        b = run_verify(w, dev=dev, handle=h)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------
+# the stages on their own, and their composition
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tree_attn_stage(dtype):
+    w = make_custom(B=3, Hq=12, Hkv=3, D=128, Lcap=1, T=29, prefix_len=[0, 0, 0], dtype=dtype, seed=21)
+    dev = to_device(w)
+    say(f"hta_tree_attn {dtype}")
+    with hta.hta_create(config_for(w)) as h:
+        o = torch.empty(w.B, w.Hq, w.T, w.D, dtype=torch.float32, device="cuda")
+        l = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device="cuda")
+        hta.hta_tree_attn(h, dev["q"], dev["k_tree"], dev["v_tree"], dev["parent"], o, l)
+        assert hta.hta_get_status(h) == 0
+    ref_o, ref_l = oracle.verify_attn(w, parts=("tree",))
+    assert np.abs(o.cpu().numpy() - ref_o).max() <= 1e-5
+    assert np.abs(l.cpu().numpy() - ref_l).max() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefix_attn_stage(dtype):
+    w = make_custom(B=3, Hq=8, Hkv=2, D=128, Lcap=2000, T=16, prefix_len=[2000, 0, 517], dtype=dtype, seed=22)
+    dev = to_device(w)
+    say(f"hta_prefix_attn {dtype}")
+    with hta.hta_create(config_for(w)) as h:
+        o = torch.empty(w.B, w.Hq, w.T, w.D, dtype=torch.float32, device="cuda")
+        l = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device="cuda")
+        hta.hta_prefix_attn(h, dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"], o, l)
+        assert hta.hta_get_status(h) == 0
+        # the same stage as two calls: split-KV kernel, then the merge of its partials
+        o2 = torch.empty_like(o)
+        l2 = torch.empty_like(l)
+        hta.hta_prefix_partials(h, dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"])
+        hta.hta_merge_prefix(h, dev["prefix_len"], o2, l2)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(l, l2)
+    o, l = o.cpu().numpy(), l.cpu().numpy()
+    ref_o, ref_l = oracle.verify_attn(w, parts=("prefix",))
+    assert np.all(l[1] == -np.inf) and np.all(o[1] == 0)
+    fin = np.isfinite(ref_l)
+    assert np.abs(o - ref_o).max() <= TOL_OUT[dtype]
+    assert (np.abs(l[fin] - ref_l[fin]) / np.maximum(1, np.abs(ref_l[fin]))).max() <= 1e-3
+
+
+def test_lse_merge_stage():
+    rng = np.random.default_rng(23)
+    B, Hq, T, D, n = 2, 4, 5, 128, 6
+    o_parts = rng.standard_normal((n, B, Hq, T, D)).astype(np.float32)
+    lse_parts = (3 * rng.standard_normal((n, B, Hq, T))).astype(np.float32)
+    lse_parts[1] = -np.inf            # an empty part
+    lse_parts[2, 0] = -np.inf
+    lse_parts[:, 1, 0, 0] = -np.inf   # a row with no part at all
+    o_parts[1] = np.nan               # an empty part's o is never read
+    ref_o, ref_l = oracle.lse_merge(list(o_parts.astype(np.float64)), list(lse_parts.astype(np.float64)))
+    say("hta_lse_merge")
+    cfg = hta.make_config(batch=B, n_q_heads=Hq, n_kv_heads=Hq, head_dim=D, tree_nodes=T, kv_capacity=1)
+    with hta.hta_create(cfg) as h:
+        o = torch.empty(B, Hq, T, D, dtype=torch.float32, device="cuda")
+        l = torch.empty(B, Hq, T, dtype=torch.float32, device="cuda")
+        hta.hta_lse_merge(h, torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda(), o, l)
+        torch.cuda.synchronize()
+    o, l = o.cpu().numpy(), l.cpu().numpy()
+    assert l[1, 0, 0] == -np.inf and np.all(o[1, 0, 0] == 0)
+    fin = np.isfinite(ref_l)
+    assert np.abs(o - ref_o).max() <= 1e-5
+    assert np.abs(l[fin] - ref_l[fin]).max() <= 1e-5
+
+
+def test_stages_compose_to_verify_attn():
+    w = make_custom(B=2, Hq=16, Hkv=4, D=128, Lcap=1234, T=20, prefix_len=[1234, 300], seed=24)
+    dev = to_device(w)
+    say("prefix + tree + merge vs verify")
+    with hta.hta_create(config_for(w)) as h:
+        f = dict(dtype=torch.float32, device="cuda")
+        op, lp = torch.empty(w.B, w.Hq, w.T, w.D, **f), torch.empty(w.B, w.Hq, w.T, **f)
+        ot, lt = torch.empty(w.B, w.Hq, w.T, w.D, **f), torch.empty(w.B, w.Hq, w.T, **f)
+        hta.hta_prefix_attn(h, dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"], op, lp)
+        hta.hta_tree_attn(h, dev["q"], dev["k_tree"], dev["v_tree"], dev["parent"], ot, lt)
+        om, lm = torch.empty(w.B, w.Hq, w.T, w.D, **f), torch.empty(w.B, w.Hq, w.T, **f)
+        hta.hta_lse_merge(h, torch.stack([op, ot]).contiguous(), torch.stack([lp, lt]).contiguous(), om, lm)
+        out, lse, status = run_verify(w, dev=dev, handle=h)
+    assert status == 0
+    assert np.abs(om.cpu().numpy() - out).max() <= 1e-2
+    assert np.abs(lm.cpu().numpy() - lse).max() <= 1e-4
+
+
+# ----------------------------------------------------------------------------
+# device-side input errors
+# ----------------------------------------------------------------------------
+
+def test_bad_tree_gives_nan_rows_and_status():
+    w = make_custom(B=3, Hq=8, Hkv=2, D=128, Lcap=300, T=10, prefix_len=[300, 200, 100], seed=31)
+    w.parent[1, 6] = 8  # a forward pointer breaks parent[i] < i
+    say("bad tree")
+    out, lse, status = run_verify(w)
+    assert status == hta.HTA_STATUS_BAD_TREE
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    good = [0, 2]
+    ref_out, ref_lse = oracle.verify_attn(w, batches=good)
+    assert_close(w, out, lse, ref_out, ref_lse)
+    cfg = config_for(w)
+    with hta.hta_create(cfg) as h:
+        mask = torch.empty(w.B, w.T, dtype=torch.int64, device="cuda")
+        hta.hta_tree_mask(h, torch.from_numpy(w.parent).cuda(), mask)
+        assert hta.hta_get_status(h) == hta.HTA_STATUS_BAD_TREE
+        assert hta.hta_get_status(h) == 0  # cleared by the read
+        assert np.all(mask.cpu().numpy()[1] == 0)
+
+
+@pytest.mark.parametrize("bad_len", [-1, 301, 1 << 30])
+def test_bad_prefix_len_gives_nan_rows_and_status(bad_len):
+    w = make_custom(B=2, Hq=8, Hkv=2, D=128, Lcap=300, T=10, prefix_len=[300, 100], seed=32)
+    w.prefix_len[1] = bad_len
+    say(f"bad prefix_len {bad_len}")
+    out, lse, status = run_verify(w)
+    assert status == hta.HTA_STATUS_BAD_PREFIX
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    ref_out, ref_lse = oracle.verify_attn(w, batches=[0])
+    assert_close(w, out, lse, ref_out, ref_lse)
