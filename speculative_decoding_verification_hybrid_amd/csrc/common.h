@@ -2,15 +2,17 @@
 //
 // Split-KV work decomposition (used by the prefix kernels and the merge
 // kernel, which must agree exactly). The cached part of every (sequence b,
-// KV head g) pair -- a "segment" -- is cut into tiles of NK tokens. All
-// tiles of all segments are laid end to end (segments in order s = b*Hkv+g)
-// and split into NWG nearly equal contiguous ranges, one per workgroup, so
-// ragged prefixes still give every compute unit the same amount of KV to
-// stream. A workgroup whose range crosses segment boundaries produces one
-// partial result per segment piece; the partial of (workgroup w, segment s)
-// lives in slot w + s, which is unique because ranges are contiguous and
-// ordered. The merge finds the workgroups that cover a segment by inverting
-// the split, so no index list is ever stored.
+// KV head g) pair -- a "segment" -- is cut into tiles of NK tokens; when the
+// tree part is fused in, each segment gets one more tile holding its tree
+// tokens (under the ancestor mask), placed last. All tiles of all segments
+// are laid end to end (segments in order s = b*Hkv+g) and split into NWG
+// nearly equal contiguous ranges, one per workgroup, so ragged prefixes still
+// give every compute unit the same amount of KV to stream. A workgroup whose
+// range crosses segment boundaries produces one partial result per segment
+// piece; the partial of (workgroup w, segment s) lives in slot w + s, which
+// is unique because ranges are contiguous and ordered. The merge finds the
+// workgroups that cover a segment by inverting the split, so no index list
+// is ever stored.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -57,36 +59,100 @@ __device__ __forceinline__ int valid_prefix(const int* prefix_len, int b, int Lc
   return (L < 0 || L > Lcap) ? 0 : L;
 }
 
-struct SplitInfo {
-  int64_t total_tiles;  // tiles over all segments
-};
-
 __device__ __forceinline__ int tiles_of(int L, int NK) { return (L + NK - 1) / NK; }
 
-__device__ inline int64_t total_tiles(const int* prefix_len, int B, int Hkv, int Lcap, int NK) {
-  int64_t t = 0;
-  for (int b = 0; b < B; ++b) t += tiles_of(valid_prefix(prefix_len, b, Lcap), NK);
-  return t * Hkv;
+// Tiles of each segment of sequence b: its prefix tiles plus tree_tiles (0 or 1).
+__device__ __forceinline__ int seg_tiles(const int* prefix_len, int b, int Lcap, int NK, int tree_tiles) {
+  return tiles_of(valid_prefix(prefix_len, b, Lcap), NK) + tree_tiles;
+}
+
+// Tile counts and split arithmetic are 32-bit: the host keeps
+// (largest possible tile count) * nwg below 2^32.
+__device__ inline unsigned total_tiles(const int* prefix_len, int B, int Hkv, int Lcap, int NK,
+                                       int tree_tiles) {
+  unsigned t = 0;
+  for (int b = 0; b < B; ++b) t += (unsigned)seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+  return t * (unsigned)Hkv;
 }
 
 // First tile (global index) owned by workgroup w of nwg.
-__device__ __forceinline__ int64_t split_begin(int64_t w, int64_t nwg, int64_t TT) {
+__device__ __forceinline__ unsigned split_begin(unsigned w, unsigned nwg, unsigned TT) {
   return (w * TT) / nwg;
 }
 
-// Workgroup owning global tile x (0 <= x < TT).
-__device__ __forceinline__ int64_t split_owner(int64_t x, int64_t nwg, int64_t TT) {
+// Workgroup owning global tile x (0 <= x < TT): the largest w with split_begin(w) <= x.
+__device__ __forceinline__ unsigned split_owner(unsigned x, unsigned nwg, unsigned TT) {
   return ((x + 1) * nwg - 1) / TT;
 }
 
 // Global index of the first tile of segment (b, g), and its tile count.
-__device__ inline void segment_tiles(const int* prefix_len, int Hkv, int Lcap, int NK, int b, int g,
-                                     int64_t* first, int* count) {
-  int64_t acc = 0;
-  for (int bb = 0; bb < b; ++bb) acc += tiles_of(valid_prefix(prefix_len, bb, Lcap), NK);
-  int nt = tiles_of(valid_prefix(prefix_len, b, Lcap), NK);
-  *first = acc * Hkv + (int64_t)g * nt;
+__device__ inline void segment_tiles(const int* prefix_len, int Hkv, int Lcap, int NK, int tree_tiles,
+                                     int b, int g, unsigned* first, int* count) {
+  unsigned acc = 0;
+  for (int bb = 0; bb < b; ++bb) acc += (unsigned)seg_tiles(prefix_len, bb, Lcap, NK, tree_tiles);
+  const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+  *first = acc * (unsigned)Hkv + (unsigned)(g * nt);
   *count = nt;
+}
+
+// Walks a workgroup's tile range segment by segment.
+struct SegmentWalk {
+  int b, g, nt;        // current sequence, KV head, tiles per segment of b
+  unsigned seq_first;  // global index of the first tile of sequence b
+};
+
+// Positions the walk on the segment holding global tile x; false if x is past the end.
+__device__ inline bool walk_start(SegmentWalk* sw, unsigned x, const int* prefix_len, int B, int Hkv,
+                                  int Lcap, int NK, int tree_tiles) {
+  unsigned first = 0;
+  for (int b = 0; b < B; ++b) {
+    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+    const unsigned span = (unsigned)nt * (unsigned)Hkv;
+    if (x < first + span) {
+      sw->b = b;
+      sw->nt = nt;
+      sw->seq_first = first;
+      sw->g = (int)((x - first) / (unsigned)nt);
+      return true;
+    }
+    first += span;
+  }
+  return false;
+}
+
+// Moves to the next segment that has tiles; false if there is none.
+__device__ inline bool walk_next(SegmentWalk* sw, const int* prefix_len, int B, int Hkv, int Lcap, int NK,
+                                 int tree_tiles) {
+  if (++sw->g < Hkv) return true;
+  sw->g = 0;
+  sw->seq_first += (unsigned)sw->nt * (unsigned)Hkv;
+  for (int b = sw->b + 1; b < B; ++b) {
+    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+    if (nt > 0) {
+      sw->b = b;
+      sw->nt = nt;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Ancestor word of tree node i from an LDS copy of its sequence's parent array:
+// bit j set iff node j is i or an ancestor of i. parent[j] < j makes the walk
+// end within T steps; a pointer that breaks -1 <= parent[j] < j clears *ok.
+__device__ inline unsigned long long ancestor_word(const int* par, int i, bool* ok) {
+  unsigned long long m = 0ull;
+  int j = i;
+  while (j >= 0) {
+    const int pj = par[j];
+    if (pj < -1 || pj >= j) {
+      *ok = false;
+      return 1ull << i;
+    }
+    m |= 1ull << j;
+    j = pj;
+  }
+  return m;
 }
 
 // XCD-aware workgroup index: MI355X hands consecutive block ids to its 8

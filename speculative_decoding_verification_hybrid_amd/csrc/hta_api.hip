@@ -16,8 +16,6 @@ struct hta_handle_s {
   hta_plan_t plan;
   void* ws;
   hta::Slots slots;
-  float* o_tree;     // [B,Hq,T,D] tree partial (normalised)
-  float* lse2_tree;  // [B,Hq,T] log2 domain
   int* err_b;        // [B] bad-tree flags of the last call
   int* status;       // sticky HTA_STATUS_* bits
 };
@@ -56,9 +54,9 @@ int validate(const hta_config_t* c) {
   return HTA_OK;
 }
 
-// Prefix-kernel shape: MFMA path blocks of 32 query rows, at most 8 per
-// workgroup (two per wave on 4 waves, or one per wave on up to 8 waves);
-// VALU path 16 rows per workgroup.
+// Split-KV kernel shape: MFMA path blocks of 32 query rows, one per wave,
+// at most 8 waves per workgroup (more rows use more row groups); VALU path
+// 16 rows per workgroup.
 void plan_rows(const hta::Dims& d, int path, hta::PrefixLaunch* pl) {
   pl->path = path;
   if (path == HTA_PATH_MFMA) {
@@ -67,13 +65,8 @@ void plan_rows(const hta::Dims& d, int path, hta::PrefixLaunch* pl) {
     const int per = (nqb + rg - 1) / rg;
     pl->row_groups = rg;
     pl->rows_per_group = per * 32;
-    if (per == 8) {
-      pl->waves = 4;
-      pl->qb = 2;
-    } else {
-      pl->waves = per;
-      pl->qb = 1;
-    }
+    pl->waves = per;
+    pl->qb = 1;
   } else {
     pl->row_groups = (d.M + 15) / 16;
     pl->rows_per_group = 16;
@@ -89,6 +82,12 @@ void plan_rows(const hta::Dims& d, int path, hta::PrefixLaunch* pl) {
   } while (0)
 
 }  // namespace
+
+static int launch_split(hta_handle_t h, const hta::PrefixInputs& in, hipStream_t s) {
+  if (h->pl.path == HTA_PATH_MFMA)
+    return check_hip(hta::launch_prefix_mfma(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
+  return check_hip(hta::launch_prefix_valu(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
+}
 
 extern "C" {
 
@@ -147,23 +146,27 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   if (nwg <= 0) {
     nwg = (int64_t)cus * (occ > 0 ? occ : 1) / h->pl.row_groups;
     nwg = nwg < 8 ? 8 : (nwg / 8) * 8;
-    const int64_t max_tiles = (int64_t)d.B * d.Hkv * ((d.Lcap + hta::kTileTokens - 1) / hta::kTileTokens);
-    if (nwg > max_tiles) nwg = max_tiles;
+    const int64_t tiles = (int64_t)d.B * d.Hkv * ((d.Lcap + hta::kTileTokens - 1) / hta::kTileTokens + 1);
+    if (nwg > tiles) nwg = tiles;
   }
+  // The kernels split tiles with 32-bit arithmetic: keep max_tiles * nwg < 2^32.
+  const int64_t max_tiles =
+      (int64_t)d.B * d.Hkv * ((d.Lcap + hta::kTileTokens - 1) / hta::kTileTokens + 1);
+  const int64_t nwg_cap = (int64_t)UINT32_MAX / max_tiles;
+  if (nwg_cap < 1) {
+    delete h;
+    return HTA_ERR_UNSUPPORTED;
+  }
+  if (nwg > nwg_cap) nwg = nwg_cap;
   if (nwg > (1 << 20)) nwg = 1 << 20;
   h->pl.nwg = (int)nwg;
 
   const int64_t max_slots = nwg + (int64_t)d.B * d.Hkv - 1;
-  const size_t rows = (size_t)d.B * d.Hq * d.T;
   size_t off = 0;
   const size_t off_so = off;
   off = align256(off + (size_t)max_slots * d.M * d.D * sizeof(float));
   const size_t off_sl = off;
   off = align256(off + (size_t)max_slots * d.M * sizeof(float));
-  const size_t off_ot = off;
-  off = align256(off + rows * d.D * sizeof(float));
-  const size_t off_lt = off;
-  off = align256(off + rows * sizeof(float));
   const size_t off_eb = off;
   off = align256(off + (size_t)d.B * sizeof(int));
   const size_t off_st = off;
@@ -176,8 +179,6 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   char* base = static_cast<char*>(h->ws);
   h->slots.o = reinterpret_cast<float*>(base + off_so);
   h->slots.lse2 = reinterpret_cast<float*>(base + off_sl);
-  h->o_tree = reinterpret_cast<float*>(base + off_ot);
-  h->lse2_tree = reinterpret_cast<float*>(base + off_lt);
   h->err_b = reinterpret_cast<int*>(base + off_eb);
   h->status = reinterpret_cast<int*>(base + off_st);
   if (hipMemset(base + off_eb, 0, off - off_eb) != hipSuccess ||
@@ -228,15 +229,10 @@ int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const vo
     return HTA_ERR_INVALID_ARG;
   if (!all_aligned(q, k_cache, v_cache, k_tree, v_tree, out)) return HTA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hta::Dims& d = h->dims;
-  HTA_TRY(check_hip(hta::launch_tree_attn(d, q, k_tree, v_tree, parent, h->o_tree, h->lse2_tree, 1.0f,
-                                          h->err_b, h->status, s)));
-  if (h->pl.path == HTA_PATH_MFMA)
-    HTA_TRY(check_hip(hta::launch_prefix_mfma(d, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s)));
-  else
-    HTA_TRY(check_hip(hta::launch_prefix_valu(d, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s)));
-  return check_hip(hta::launch_merge_slots(d, h->pl.nwg, prefix_len, h->slots, h->o_tree, h->lse2_tree,
-                                           h->err_b, out, d.bf16, lse, h->status, s));
+  const hta::PrefixInputs in = {q, k_cache, v_cache, k_tree, v_tree, parent, prefix_len};
+  HTA_TRY(launch_split(h, in, s));
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, 1, prefix_len, h->slots, h->err_b, out,
+                                           h->dims.bf16, lse, h->status, s));
 }
 
 int hta_tree_mask(hta_handle_t h, const int32_t* parent, uint64_t* mask_out, void* stream) {
@@ -266,19 +262,16 @@ int hta_prefix_partials(hta_handle_t h, const void* q, const void* k_cache, cons
                         const int32_t* prefix_len, void* stream) {
   if (!h || !q || !k_cache || !v_cache || !prefix_len) return HTA_ERR_INVALID_ARG;
   if (!all_aligned(q, k_cache, v_cache)) return HTA_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (h->pl.path == HTA_PATH_MFMA)
-    return check_hip(hta::launch_prefix_mfma(h->dims, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s));
-  return check_hip(hta::launch_prefix_valu(h->dims, h->pl, q, k_cache, v_cache, prefix_len, h->slots, s));
+  const hta::PrefixInputs in = {q, k_cache, v_cache, nullptr, nullptr, nullptr, prefix_len};
+  return launch_split(h, in, static_cast<hipStream_t>(stream));
 }
 
 int hta_merge_prefix(hta_handle_t h, const int32_t* prefix_len, float* o_prefix, float* lse_prefix,
                      void* stream) {
   if (!h || !prefix_len || !o_prefix || !lse_prefix) return HTA_ERR_INVALID_ARG;
   if (!all_aligned(o_prefix)) return HTA_ERR_INVALID_ARG;
-  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, prefix_len, h->slots, nullptr, nullptr,
-                                           nullptr, o_prefix, false, lse_prefix, h->status,
-                                           static_cast<hipStream_t>(stream)));
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, 0, prefix_len, h->slots, nullptr, o_prefix,
+                                           false, lse_prefix, h->status, static_cast<hipStream_t>(stream)));
 }
 
 int hta_lse_merge(hta_handle_t h, int32_t n_parts, const float* o_parts, const float* lse_parts,

@@ -31,13 +31,26 @@ struct PrefixLaunch {
   int qb;             // MFMA: q-blocks per wave
 };
 
-// Prefix part, split-KV: writes slots.
-hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const void* q,
-                              const void* k_cache, const void* v_cache, const int* prefix_len,
-                              Slots slots, hipStream_t s);
-hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const void* q,
-                              const void* k_cache, const void* v_cache, const int* prefix_len,
-                              Slots slots, hipStream_t s);
+// Inputs of the split-KV kernels. With k_tree/v_tree/parent set, each
+// (sequence, KV head) gets one extra tile of tree tokens under the ancestor
+// mask (the fused tree part); with them null only the cached part is done.
+struct PrefixInputs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const void* k_tree;
+  const void* v_tree;
+  const int* parent;
+  const int* prefix_len;
+};
+
+// Split-KV kernels: write one partial per (workgroup, segment piece) to slots.
+// With the tree fused in, the workgroup holding the tree tile of (b, KV head 0)
+// writes err_b[b] (1 if parent[] of b is malformed) and raises the status bit.
+hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
+                              int* err_b, int* status, hipStream_t s);
+hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
+                              int* err_b, int* status, hipStream_t s);
 // Occupancy (workgroups per CU) of the chosen prefix kernel, for sizing nwg.
 int prefix_mfma_occupancy(int D, int waves, int qb);
 int prefix_valu_occupancy(int D, bool bf16);
@@ -51,11 +64,12 @@ hipError_t launch_tree_attn(const Dims& d, const void* q, const void* k_tree, co
 hipError_t launch_tree_mask(const Dims& d, const int* parent, uint64_t* mask_out, int* status,
                             hipStream_t s);
 
-// Merge of the prefix slots (+ optional tree partial) into out (float or bf16)
-// and natural-log lse.
-hipError_t launch_merge_slots(const Dims& d, int nwg, const int* prefix_len, Slots slots,
-                              const float* o_tree, const float* lse2_tree, const int* err_b,
-                              void* out, bool out_bf16, float* lse, int* status, hipStream_t s);
+// Merge of the slots of one split-KV launch (tree_tiles as in that launch)
+// into out (float or bf16) and natural-log lse; err_b (may be null) marks
+// sequences whose rows become NaN.
+hipError_t launch_merge_slots(const Dims& d, int nwg, int tree_tiles, const int* prefix_len, Slots slots,
+                              const int* err_b, void* out, bool out_bf16, float* lse, int* status,
+                              hipStream_t s);
 // Merge of n_parts caller-provided partials (natural-log LSE) into float out.
 hipError_t launch_merge_parts(const Dims& d, int n_parts, const float* o_parts,
                               const float* lse_parts, float* out, float* lse, hipStream_t s);

@@ -10,7 +10,8 @@
 // natural log.
 //
 // 32 threads per row, each owning D/32 consecutive dims (16-byte loads for
-// D = 128), 8 rows per 256-thread workgroup.
+// D = 128), 8 rows per 256-thread workgroup. The weighted pass is unrolled
+// and branch-free so that the loads of several parts are in flight together.
 #include "common.h"
 #include "hta_internal.h"
 
@@ -18,17 +19,16 @@ namespace hta {
 namespace {
 
 constexpr int NK = kTileTokens;
+constexpr int UNROLL = 8;
 
 struct MergeArgs {
-  // slot mode: partials of the prefix kernel + optional tree partial
+  // slot mode: partials of one split-KV launch
   const int* prefix_len;
   const float* slot_o;
   const float* slot_lse2;
-  const float* o_tree;
-  const float* lse2_tree;
   const int* err_b;
   int* status;
-  int nwg;
+  int nwg, tree_tiles;
   // parts mode: n_parts caller arrays, natural-log lse
   const float* o_parts;
   const float* lse_parts;
@@ -67,53 +67,55 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   const int r = (h - g * a.G) * a.T + node;  // row within the KV head's M rows
 
   bool bad = false;
-  int p_first = 0, p_count = 0;  // slot range (SLOTS) or part range
-  int64_t w_first = 0, TT = 1;   // SLOTS: first workgroup of the range, total tiles
-  bool with_tree = false;
+  int p_count = 0;
+  unsigned w_first = 0, TT = 1;
+  const float* o_base;
+  const float* l_base;
+  size_t o_stride, l_stride;
+  float l_scale;
   if (SLOTS) {
     const int Lraw = a.prefix_len[b];
     const bool bad_prefix = Lraw < 0 || Lraw > a.Lcap;
     bad = bad_prefix || (a.err_b != nullptr && a.err_b[b] != 0);
     if (bad_prefix && h == 0 && node == 0 && dq == 0) atomicOr(a.status, kStatusBadPrefix);
-    TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK);
-    int64_t first;
+    TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles);
+    unsigned first;
     int count;
-    segment_tiles(a.prefix_len, a.Hkv, a.Lcap, NK, b, g, &first, &count);
+    segment_tiles(a.prefix_len, a.Hkv, a.Lcap, NK, a.tree_tiles, b, g, &first, &count);
+    int p_first = 0;
     if (count > 0) {
-      const int64_t wf = split_owner(first, a.nwg, TT);
-      const int64_t wl = split_owner(first + count - 1, a.nwg, TT);
-      p_first = (int)wf + b * a.Hkv + g;
-      p_count = (int)(wl - wf) + 1;
-      w_first = wf;
+      w_first = split_owner(first, a.nwg, TT);
+      const unsigned wl = split_owner(first + (unsigned)count - 1, a.nwg, TT);
+      p_first = (int)w_first + b * a.Hkv + g;
+      p_count = (int)(wl - w_first) + 1;
     }
-    with_tree = a.o_tree != nullptr;
+    o_base = a.slot_o + ((size_t)p_first * a.M + r) * D + dq * DV;
+    l_base = a.slot_lse2 + (size_t)p_first * a.M + r;
+    o_stride = (size_t)a.M * D;
+    l_stride = (size_t)a.M;
+    l_scale = 1.0f;
   } else {
-    p_first = 0;
     p_count = a.n_parts;
+    o_base = a.o_parts + (size_t)row * D + dq * DV;
+    l_base = a.lse_parts + row;
+    o_stride = (size_t)rows_total * D;
+    l_stride = (size_t)rows_total;
+    l_scale = kLog2e;
   }
 
-  // With more workgroups than tiles some workgroups own no tile; they sit
-  // between the owners of a segment's first and last tile and wrote nothing.
+  // LSE of part k in log2 units; -inf for an empty part. With more workgroups
+  // than tiles some workgroups own no tile: they sit between the owners of a
+  // segment's first and last tile and wrote nothing to their slot.
   auto part_lse2 = [&](int k) -> float {
     if (SLOTS) {
-      const int64_t w = w_first + k;
-      if (split_begin(w, a.nwg, TT) == split_begin(w + 1, a.nwg, TT)) return -__builtin_inff();
-      return a.slot_lse2[(size_t)(p_first + k) * a.M + r];
+      const unsigned wk = w_first + (unsigned)k;
+      if (split_begin(wk, a.nwg, TT) == split_begin(wk + 1, a.nwg, TT)) return -__builtin_inff();
     }
-    return a.lse_parts[(size_t)k * rows_total + row] * kLog2e;
-  };
-  auto part_o = [&](int k) -> const float* {
-    if (SLOTS) return a.slot_o + ((size_t)(p_first + k) * a.M + r) * D;
-    return a.o_parts + ((size_t)k * rows_total + row) * D;
+    return l_base[(size_t)k * l_stride] * l_scale;
   };
 
   float mx = -__builtin_inff();
   for (int k = 0; k < p_count; ++k) mx = fmaxf(mx, part_lse2(k));
-  float lt2 = -__builtin_inff();
-  if (with_tree) {
-    lt2 = a.lse2_tree[row];
-    mx = fmaxf(mx, lt2);
-  }
 
   float acc[DV];
 #pragma unroll
@@ -123,21 +125,22 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     lse_out = -__builtin_inff();
   } else {
     float sum = 0.f;
-    for (int k = 0; k < p_count; ++k) {
-      const float lk = part_lse2(k);
-      if (lk == -__builtin_inff()) continue;  // empty part: its o is never read
-      const float wk = fast_exp2(lk - mx);
-      const VT ov = *(const VT*)(part_o(k) + dq * DV);
-      sum += wk;
+    for (int k0 = 0; k0 < p_count; k0 += UNROLL) {
+      float wk[UNROLL];
+      VT ov[UNROLL];
 #pragma unroll
-      for (int e = 0; e < DV; ++e) acc[e] = fmaf(wk, ov[e], acc[e]);
-    }
-    if (with_tree) {
-      const float wk = fast_exp2(lt2 - mx);
-      const VT ov = *(const VT*)(a.o_tree + (size_t)row * D + dq * DV);
-      sum += wk;
+      for (int u = 0; u < UNROLL; ++u) {
+        const int k = min(k0 + u, p_count - 1);  // in-bounds load; weight 0 past the end
+        const float lk = part_lse2(k);
+        wk[u] = (k0 + u < p_count && lk != -__builtin_inff()) ? fast_exp2(lk - mx) : 0.f;
+        ov[u] = *(const VT*)(o_base + (size_t)k * o_stride);
+      }
 #pragma unroll
-      for (int e = 0; e < DV; ++e) acc[e] = fmaf(wk, ov[e], acc[e]);
+      for (int u = 0; u < UNROLL; ++u) {
+        sum += wk[u];
+#pragma unroll
+        for (int e = 0; e < DV; ++e) acc[e] += wk[u] == 0.f ? 0.f : wk[u] * ov[u][e];
+      }
     }
     const float inv = 1.0f / sum;
 #pragma unroll
@@ -192,20 +195,19 @@ unsigned grid_for(const Dims& d) {
 
 }  // namespace
 
-hipError_t launch_merge_slots(const Dims& d, int nwg, const int* prefix_len, Slots slots,
-                              const float* o_tree, const float* lse2_tree, const int* err_b,
-                              void* out, bool out_bf16, float* lse, int* status, hipStream_t s) {
+hipError_t launch_merge_slots(const Dims& d, int nwg, int tree_tiles, const int* prefix_len, Slots slots,
+                              const int* err_b, void* out, bool out_bf16, float* lse, int* status,
+                              hipStream_t s) {
   MergeFn k = out_bf16 ? pick<true, true>(d.D) : pick<true, false>(d.D);
   if (!k) return hipErrorInvalidValue;
   MergeArgs a = base_args(d);
   a.prefix_len = prefix_len;
   a.slot_o = slots.o;
   a.slot_lse2 = slots.lse2;
-  a.o_tree = o_tree;
-  a.lse2_tree = lse2_tree;
   a.err_b = err_b;
   a.status = status;
   a.nwg = nwg;
+  a.tree_tiles = tree_tiles;
   a.out = out;
   a.lse = lse;
   hipLaunchKernelGGL(k, dim3(grid_for(d)), dim3(256), 0, s, a);

@@ -15,22 +15,6 @@
 namespace hta {
 namespace {
 
-// Ancestor word of node i from an LDS copy of the sequence's parent array.
-__device__ inline unsigned long long ancestor_word(const int* par, int i, bool* ok) {
-  unsigned long long m = 0ull;
-  int j = i;
-  while (j >= 0) {
-    const int pj = par[j];
-    if (pj < -1 || pj >= j) {
-      *ok = false;
-      return 0ull;
-    }
-    m |= 1ull << j;
-    j = pj;
-  }
-  return m;
-}
-
 __global__ void __launch_bounds__(64) tree_mask_kernel(const int* parent, unsigned long long* out,
                                                        int* status, int T) {
   __shared__ int par[64];
