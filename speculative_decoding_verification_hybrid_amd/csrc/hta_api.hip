@@ -164,7 +164,8 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   const int64_t max_slots = nwg + (int64_t)d.B * d.Hkv - 1;
   size_t off = 0;
   const size_t off_so = off;
-  off = align256(off + (size_t)max_slots * d.M * d.D * sizeof(float));
+  const bool slot_bf16 = path == HTA_PATH_MFMA;
+  off = align256(off + (size_t)max_slots * d.M * d.D * (slot_bf16 ? 2 : 4));
   const size_t off_sl = off;
   off = align256(off + (size_t)max_slots * d.M * sizeof(float));
   const size_t off_eb = off;
@@ -177,7 +178,8 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
     return HTA_ERR_NO_MEMORY;
   }
   char* base = static_cast<char*>(h->ws);
-  h->slots.o = reinterpret_cast<float*>(base + off_so);
+  h->slots.o = base + off_so;
+  h->slots.o_bf16 = slot_bf16;
   h->slots.lse2 = reinterpret_cast<float*>(base + off_sl);
   h->err_b = reinterpret_cast<int*>(base + off_eb);
   h->status = reinterpret_cast<int*>(base + off_st);

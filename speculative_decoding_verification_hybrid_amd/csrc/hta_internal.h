@@ -15,11 +15,13 @@ struct Dims {
   float scale_log2;                  // softmax scale * log2(e)
 };
 
-// Partial results of the prefix kernels: slot s holds M rows of D floats
-// (normalised output) and M log2-domain LSE values.
+// Partial results of the split-KV kernels: slot s holds M rows of D values
+// (normalised output; bf16 from the MFMA path, float from the VALU path) and
+// M log2-domain LSE values (float).
 struct Slots {
-  float* o;
+  void* o;
   float* lse2;
+  bool o_bf16;
 };
 
 struct PrefixLaunch {

@@ -3,15 +3,15 @@
 // log-sum-exp trick, which keeps the result exact).
 //
 // For one output row with partials (o_k normalised, lse_k) over disjoint key
-// sets: lse = log2(sum_k 2^lse_k) and out = sum_k 2^(lse_k - lse) o_k, done
-// as one max pass over the lse values and one weighted pass over the o rows.
-// Parts with lse_k = -inf contribute nothing; a row with no part at all gets
+// sets: lse = log2(sum_k 2^lse_k) and out = sum_k 2^(lse_k - lse) o_k. Parts
+// with lse_k = -inf contribute nothing; a row with no part at all gets
 // out = 0, lse = -inf. Internally every LSE is base 2; the stored lse is
 // natural log.
 //
-// 32 threads per row, each owning D/32 consecutive dims (16-byte loads for
-// D = 128), 8 rows per 256-thread workgroup. The weighted pass is unrolled
-// and branch-free so that the loads of several parts are in flight together.
+// One wave per output row. Its 64 lanes are PG part groups x (D/8) lanes of
+// 8 dims: part group p takes parts p, p+PG, p+2PG, ... and keeps its own
+// running max and weighted sum, so each lane has up to 8 independent loads in
+// flight; the groups are then combined with cross-lane exchanges.
 #include "common.h"
 #include "hta_internal.h"
 
@@ -24,7 +24,7 @@ constexpr int UNROLL = 8;
 struct MergeArgs {
   // slot mode: partials of one split-KV launch
   const int* prefix_len;
-  const float* slot_o;
+  const void* slot_o;
   const float* slot_lse2;
   const int* err_b;
   int* status;
@@ -39,25 +39,30 @@ struct MergeArgs {
   int B, Hq, Hkv, G, T, Lcap, M;
 };
 
-template <int D>
-struct Vec;
-template <>
-struct Vec<128> {
-  typedef f32x4 T;
-};
-template <>
-struct Vec<64> {
-  typedef float __attribute__((ext_vector_type(2))) T;
-};
+// 8 consecutive elements of a partial row as floats.
+__device__ __forceinline__ void load8(const float* p, float* o) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+  o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
+  o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
+}
+__device__ __forceinline__ void load8(const unsigned short* p, float* o) {
+  const u32x4 a = *(const u32x4*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(a[i] << 16);
+    o[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+  }
+}
 
-template <int D, bool SLOTS, bool OUT_BF16>
+template <int D, bool SLOTS, typename TSlot, bool OUT_BF16>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  constexpr int DV = D / 32;
-  typedef typename Vec<D>::T VT;
-  const int tid = threadIdx.x;
-  const int dq = tid & 31;
+  constexpr int LPR = D / 8;   // lanes per part group (8 dims each)
+  constexpr int PG = 64 / LPR;  // part groups per row
+  const int lane = threadIdx.x & 63;
+  const int pg = lane / LPR;
+  const int dl = lane % LPR;
   const int64_t rows_total = (int64_t)a.B * a.Hq * a.T;
-  const int64_t row = (int64_t)blockIdx.x * 8 + (tid >> 5);
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows_total) return;
   const int b = (int)(row / ((int64_t)a.Hq * a.T));
   const int rem = (int)(row % ((int64_t)a.Hq * a.T));
@@ -69,7 +74,8 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   bool bad = false;
   int p_count = 0;
   unsigned w_first = 0, TT = 1;
-  const float* o_base;
+  bool maybe_empty = false;
+  const TSlot* o_base;
   const float* l_base;
   size_t o_stride, l_stride;
   float l_scale;
@@ -77,7 +83,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     const int Lraw = a.prefix_len[b];
     const bool bad_prefix = Lraw < 0 || Lraw > a.Lcap;
     bad = bad_prefix || (a.err_b != nullptr && a.err_b[b] != 0);
-    if (bad_prefix && h == 0 && node == 0 && dq == 0) atomicOr(a.status, kStatusBadPrefix);
+    if (bad_prefix && h == 0 && node == 0 && lane == 0) atomicOr(a.status, kStatusBadPrefix);
     TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles);
     unsigned first;
     int count;
@@ -89,90 +95,109 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
       p_first = (int)w_first + b * a.Hkv + g;
       p_count = (int)(wl - w_first) + 1;
     }
-    o_base = a.slot_o + ((size_t)p_first * a.M + r) * D + dq * DV;
+    // with more workgroups than tiles, some own no tile and wrote nothing
+    maybe_empty = TT < (unsigned)a.nwg;
+    o_base = static_cast<const TSlot*>(a.slot_o) + ((size_t)p_first * a.M + r) * D + dl * 8;
     l_base = a.slot_lse2 + (size_t)p_first * a.M + r;
     o_stride = (size_t)a.M * D;
     l_stride = (size_t)a.M;
     l_scale = 1.0f;
   } else {
     p_count = a.n_parts;
-    o_base = a.o_parts + (size_t)row * D + dq * DV;
+    o_base = reinterpret_cast<const TSlot*>(a.o_parts) + (size_t)row * D + dl * 8;
     l_base = a.lse_parts + row;
     o_stride = (size_t)rows_total * D;
     l_stride = (size_t)rows_total;
     l_scale = kLog2e;
   }
 
-  // LSE of part k in log2 units; -inf for an empty part. With more workgroups
-  // than tiles some workgroups own no tile: they sit between the owners of a
-  // segment's first and last tile and wrote nothing to their slot.
-  auto part_lse2 = [&](int k) -> float {
-    if (SLOTS) {
-      const unsigned wk = w_first + (unsigned)k;
-      if (split_begin(wk, a.nwg, TT) == split_begin(wk + 1, a.nwg, TT)) return -__builtin_inff();
-    }
-    return l_base[(size_t)k * l_stride] * l_scale;
-  };
-
-  float mx = -__builtin_inff();
-  for (int k = 0; k < p_count; ++k) mx = fmaxf(mx, part_lse2(k));
-
-  float acc[DV];
+  // This lane's part group: running max m, weighted sum s and accumulator acc.
+  float m = -__builtin_inff(), s = 0.f, acc[8];
 #pragma unroll
-  for (int e = 0; e < DV; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int k0 = pg; k0 < p_count; k0 += PG * UNROLL) {
+    float lk[UNROLL], ov[UNROLL][8];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int k = min(k0 + u * PG, p_count - 1);  // in-bounds; ignored past the end
+      float l = l_base[(size_t)k * l_stride] * l_scale;
+      if (k0 + u * PG >= p_count) l = -__builtin_inff();
+      if (SLOTS && maybe_empty) {
+        const unsigned wk = w_first + (unsigned)k;
+        if (split_begin(wk, a.nwg, TT) == split_begin(wk + 1, a.nwg, TT)) l = -__builtin_inff();
+      }
+      lk[u] = l;
+      load8(o_base + (size_t)k * o_stride, ov[u]);
+    }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) mc = fmaxf(mc, lk[u]);
+    if (mc != -__builtin_inff()) {
+      const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mc);
+      s *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const bool live = lk[u] != -__builtin_inff();  // an empty part's o is never used
+        const float wk = live ? fast_exp2(lk[u] - mc) : 0.f;
+        s += wk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += live ? wk * ov[u][e] : 0.f;
+      }
+      m = mc;
+    }
+  }
+  // Combine the part groups (lanes dl, dl + LPR, ... hold the same dims).
+  float mt = m;
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+  const float sc = (m == -__builtin_inff()) ? 0.f : fast_exp2(m - mt);
+  s *= sc;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    s += __shfl_xor(s, off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
   float lse_out;
-  if (mx == -__builtin_inff()) {
+  if (mt == -__builtin_inff()) {
     lse_out = -__builtin_inff();
   } else {
-    float sum = 0.f;
-    for (int k0 = 0; k0 < p_count; k0 += UNROLL) {
-      float wk[UNROLL];
-      VT ov[UNROLL];
+    const float inv = 1.0f / s;
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int k = min(k0 + u, p_count - 1);  // in-bounds load; weight 0 past the end
-        const float lk = part_lse2(k);
-        wk[u] = (k0 + u < p_count && lk != -__builtin_inff()) ? fast_exp2(lk - mx) : 0.f;
-        ov[u] = *(const VT*)(o_base + (size_t)k * o_stride);
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        sum += wk[u];
-#pragma unroll
-        for (int e = 0; e < DV; ++e) acc[e] += wk[u] == 0.f ? 0.f : wk[u] * ov[u][e];
-      }
-    }
-    const float inv = 1.0f / sum;
-#pragma unroll
-    for (int e = 0; e < DV; ++e) acc[e] *= inv;
-    lse_out = (mx + fast_log2(sum)) * kLn2;
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    lse_out = (mt + fast_log2(s)) * kLn2;
   }
   if (bad) {
-    const float nan = __builtin_nanf("");
 #pragma unroll
-    for (int e = 0; e < DV; ++e) acc[e] = nan;
-    lse_out = nan;
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_nanf("");
+    lse_out = __builtin_nanf("");
   }
+  if (pg != 0) return;
   if (OUT_BF16) {
-    unsigned short* op = static_cast<unsigned short*>(a.out) + (size_t)row * D + dq * DV;
+    u32x4 pk;
 #pragma unroll
-    for (int e = 0; e < DV; ++e) op[e] = float_to_bf16_bits(acc[e]);
+    for (int i = 0; i < 4; ++i)
+      pk[i] = (unsigned)float_to_bf16_bits(acc[2 * i]) | ((unsigned)float_to_bf16_bits(acc[2 * i + 1]) << 16);
+    *(u32x4*)(static_cast<unsigned short*>(a.out) + (size_t)row * D + dl * 8) = pk;
   } else {
-    float* op = static_cast<float*>(a.out) + (size_t)row * D + dq * DV;
-    VT v;
-#pragma unroll
-    for (int e = 0; e < DV; ++e) v[e] = acc[e];
-    *(VT*)op = v;
+    float* op = static_cast<float*>(a.out) + (size_t)row * D + dl * 8;
+    f32x4 v0 = {acc[0], acc[1], acc[2], acc[3]}, v1 = {acc[4], acc[5], acc[6], acc[7]};
+    *(f32x4*)op = v0;
+    *(f32x4*)(op + 4) = v1;
   }
-  if (dq == 0) a.lse[row] = lse_out;
+  if (dl == 0) a.lse[row] = lse_out;
 }
 
 typedef void (*MergeFn)(MergeArgs);
 
-template <bool SLOTS, bool OUT_BF16>
+template <bool SLOTS, typename TSlot, bool OUT_BF16>
 MergeFn pick(int D) {
-  if (D == 128) return merge_kernel<128, SLOTS, OUT_BF16>;
-  if (D == 64) return merge_kernel<64, SLOTS, OUT_BF16>;
+  if (D == 128) return merge_kernel<128, SLOTS, TSlot, OUT_BF16>;
+  if (D == 64) return merge_kernel<64, SLOTS, TSlot, OUT_BF16>;
   return nullptr;
 }
 
@@ -190,7 +215,7 @@ MergeArgs base_args(const Dims& d) {
 
 unsigned grid_for(const Dims& d) {
   const int64_t rows = (int64_t)d.B * d.Hq * d.T;
-  return (unsigned)((rows + 7) / 8);
+  return (unsigned)((rows + 3) / 4);
 }
 
 }  // namespace
@@ -198,7 +223,11 @@ unsigned grid_for(const Dims& d) {
 hipError_t launch_merge_slots(const Dims& d, int nwg, int tree_tiles, const int* prefix_len, Slots slots,
                               const int* err_b, void* out, bool out_bf16, float* lse, int* status,
                               hipStream_t s) {
-  MergeFn k = out_bf16 ? pick<true, true>(d.D) : pick<true, false>(d.D);
+  MergeFn k;
+  if (slots.o_bf16)
+    k = out_bf16 ? pick<true, unsigned short, true>(d.D) : pick<true, unsigned short, false>(d.D);
+  else
+    k = out_bf16 ? pick<true, float, true>(d.D) : pick<true, float, false>(d.D);
   if (!k) return hipErrorInvalidValue;
   MergeArgs a = base_args(d);
   a.prefix_len = prefix_len;
@@ -216,7 +245,7 @@ hipError_t launch_merge_slots(const Dims& d, int nwg, int tree_tiles, const int*
 
 hipError_t launch_merge_parts(const Dims& d, int n_parts, const float* o_parts,
                               const float* lse_parts, float* out, float* lse, hipStream_t s) {
-  MergeFn k = pick<false, false>(d.D);
+  MergeFn k = pick<false, float, false>(d.D);
   if (!k) return hipErrorInvalidValue;
   MergeArgs a = base_args(d);
   a.o_parts = o_parts;

@@ -15,9 +15,9 @@
 //
 // Per workgroup: WQ waves, each owning one block of 32 query rows (two waves
 // per SIMD at WQ = 8, so one wave's softmax overlaps the other's MFMA). Per
-// tile, all waves share one copy of K and V in LDS, both row-major with each
-// row's 16-byte chunks XOR-swizzled so that the reads below are free of bank
-// conflicts:
+// tile, all waves share one copy of K and V in LDS, both row-major. K rows are
+// padded by 16 bytes and V rows by 64 bytes, which makes the reads below free
+// of bank conflicts while every read is a base register plus an immediate:
 //   * scores are computed transposed, S^T = K . Q^T: each lane holds one
 //     query row (a column of the MFMA result) and 16 tokens, so the row max
 //     needs one cross-half exchange and the running (m, l) live in lanes;
@@ -51,7 +51,7 @@ struct PrefixArgs {
   const unsigned short* vt;
   const int* parent;
   const int* prefix_len;
-  float* slot_o;
+  unsigned short* slot_o;  // bf16 partials
   float* slot_lse2;
   int* err_b;
   int* status;
@@ -60,13 +60,25 @@ struct PrefixArgs {
   float scale_log2;
 };
 
-// XOR swizzle of the 16-byte chunks of tile row r: D = 128 rows span all 64
-// banks, D = 64 rows half of them. Conflict-free for the 16 distinct rows of a
-// K read and for the 4 rows x 4 chunks of a transposed V read.
+// LDS row strides (bf16 elements). K: 16-byte pad, so the 16 rows of a K
+// fragment read start 4 banks apart. V: 64-byte pad, so the 4 rows x 4 chunks
+// of a transposed V read cover all 64 banks once (D = 128: rows 16 banks
+// apart; D = 64: rows 48 banks apart).
 template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+struct Rows {
+  static constexpr int K = D + 8;
+  static constexpr int V = D + 32;
+};
+
+// Cross-half (lane l <-> l ^ 32) max and sum in VALU: the two results of the
+// lane swap are this lane's value and its partner's, in some order.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(fmaxf(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // MFMA row -> token within a 32-token sub-tile: swap bits 2 and 3.
@@ -76,17 +88,25 @@ __device__ __forceinline__ i16x4 lds_read_tr(const unsigned short* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// Threads per workgroup: the WQ compute waves plus loader-only waves up to 4
+// (WQ <= 4) or 8, so no wave stages more than 8 chunks of a tile.
+template <int WQ>
+constexpr int threads_for() { return WQ <= 4 ? 256 : 512; }
+
 template <int D, int WQ>
-__global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
-  constexpr int NT = 64 * WQ;
+__global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixArgs a) {
+  constexpr int NT = threads_for<WQ>();
   constexpr int KC = D / 16;          // k-chunks of K.Q^T
   constexpr int DB = D / 32;          // 32-dim blocks of O
   constexpr int DCH = D / 8;          // 16-byte chunks per row
-  constexpr int TILE = NK * D;        // bf16 elements of one K (or V) tile
-  constexpr int CH = 2 * NK * DCH;    // chunks of K + V per tile
+  constexpr int KR = Rows<D>::K, VR = Rows<D>::V;
+  constexpr int KT = NK * KR;         // bf16 elements of one K tile
+  constexpr int STAGE = KT + NK * VR; // K tile + V tile
+  constexpr int CH = 2 * NK * DCH;    // 16-byte chunks of K + V per tile
   constexpr int NL = (CH + NT - 1) / NT;
+  static_assert(2 * STAGE >= WQ * 32 * D, "epilogue staging reuses the tile buffers");
 
-  __shared__ __attribute__((aligned(16))) unsigned short lds[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) unsigned short lds[2 * STAGE];
   __shared__ int par_s[64];
   __shared__ unsigned long long anc_s[64];
   __shared__ int bad_s;
@@ -108,9 +128,10 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
   SegmentWalk sw;
   if (!walk_start(&sw, x, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles)) return;
 
+  const bool computes = wave < WQ;  // loader-only waves stage tiles and hit the barriers
   const int row = blockIdx.y * a.rows_per_group + wave * 32 + l32;  // this lane's query row
   const int row_limit = min(a.M, (int)(blockIdx.y + 1) * a.rows_per_group);
-  const bool row_ok = row < row_limit;
+  const bool row_ok = computes && row < row_limit;
   const int node = row_ok ? row % a.T : 0;
 
   while (true) {
@@ -172,7 +193,7 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
       }
     };
     auto store_tile = [&](int stage) {
-      unsigned short* base = lds + stage * 2 * TILE;
+      unsigned short* base = lds + stage * STAGE;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int idx = tid + i * NT;
@@ -180,7 +201,7 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
           const int is_v = idx >= NK * DCH;
           const int e = idx - is_v * NK * DCH;
           const int r = e / DCH, c = e % DCH;
-          *(u32x4*)(base + is_v * TILE + r * D + ((c ^ swz<D>(r)) << 3)) = reg[i];
+          *(u32x4*)(base + (is_v ? KT + r * VR : r * KR) + c * 8) = reg[i];
         }
       }
     };
@@ -201,24 +222,27 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
     for (int t = 0; t < ntiles; ++t) {
       const int ti = tile0 + t;
       if (t + 1 < ntiles) load_tile(ti + 1);
-      const unsigned short* Ks = lds + (t & 1) * 2 * TILE;
-      const unsigned short* Vs = Ks + TILE;
+      const unsigned short* Ks = lds + (t & 1) * STAGE;
+      const unsigned short* Vs = Ks + KT;
       const bool tree = ti >= n_prefix;
       const int nvalid = tree ? a.T : min(NK, L - ti * NK);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        if (st * 32 >= nvalid) break;
+        if (!computes || st * 32 >= nvalid) break;
+        // S^T = K . Q^T for 32 tokens: fetch all 8 K fragments, then the MFMA chain.
+        const unsigned short* krow = Ks + (st * 32 + kperm(l32)) * KR + 8 * hh;
+        bf16x8 ka[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) ka[c] = *(const bf16x8*)(krow + 16 * c);
         f32x16 S;
 #pragma unroll
         for (int v = 0; v < 16; ++v) S[v] = 0.f;
-        const int kr = st * 32 + kperm(l32);
-        const unsigned short* krow = Ks + kr * D;
-        const int ksw = swz<D>(kr);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const bf16x8 ka = *(const bf16x8*)(krow + (((2 * c + hh) ^ ksw) << 3));
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], S, 0, 0, 0);
-        }
+        for (int c = 0; c < KC; ++c) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], S, 0, 0, 0);
+        // keep the K reads ahead of the chain (the scheduler would otherwise sink
+        // each read next to its MFMA and pay the LDS latency 8 times)
+        __builtin_amdgcn_sched_group_barrier(0x100, KC, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, KC, 0);  // MFMAs
         // S[v] scores token st*32 + 16*(v/8) + 8*hh + v%8 of the tile. On the
         // tree tile and on a ragged last tile, bit v of `vis` says whether that
         // token is seen; hidden scores get -inf added (no compares, no masks).
@@ -235,11 +259,11 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
           for (int v = 0; v < 16; ++v)
             S[v] += __uint_as_float((((vis >> v) & 1u) - 1u) & 0xff800000u);
         }
-        float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);
-#pragma unroll
-        for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, S[v]), S[v + 1]);
-        mx = fmaxf(mx, S[15]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        float mx0 = fmaxf(fmaxf(S[0], S[1]), S[2]), mx1 = fmaxf(fmaxf(S[3], S[4]), S[5]);
+        float mx2 = fmaxf(fmaxf(S[6], S[7]), S[8]), mx3 = fmaxf(fmaxf(S[9], S[10]), S[11]);
+        float mx4 = fmaxf(fmaxf(S[12], S[13]), S[14]);
+        float mx = fmaxf(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3)), fmaxf(mx4, S[15]));
+        mx = half_max(mx) * a.scale_log2;
         if (__any(mx > m + 8.0f)) {
           const float mn = fmaxf(m, mx);
           const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mn);
@@ -250,29 +274,30 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
         }
         const float nm = m == -__builtin_inff() ? 0.f : -m;
         bf16x8 P[2];
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = fast_exp2(fmaf(S[v], a.scale_log2, nm));
-          l += p;
+          ls[v & 3] += p;
           P[v >> 3][v & 7] = (__bf16)p;
         }
+        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
         // O^T += V^T . P^T over the two 16-token k-chunks of this sub-tile.
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; ++kc2) {
-          const int vr = st * 32 + 16 * kc2 + 8 * hh + (gl >> 2);  // rows vr and vr + 4
-          const unsigned short* vrow0 = Vs + vr * D;
-          const unsigned short* vrow1 = vrow0 + 4 * D;
-          const int sw0 = swz<D>(vr), sw1 = swz<D>(vr + 4);
+          // rows vr and vr + 4 of the tile; dims of this lane's 4-dim group
+          const int vr = st * 32 + 16 * kc2 + 8 * hh + (gl >> 2);
+          const unsigned short* vp0 = Vs + vr * VR + 16 * (grp & 1) + 4 * (gl & 3);
+          bf16x8 va[DB];
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int dcol = db * 32 + 16 * (grp & 1) + 4 * (gl & 3);
-            const int ch = dcol >> 3, half = (dcol >> 2) & 1;
-            const i16x4 lo = lds_read_tr(vrow0 + (((ch ^ sw0) << 3) | (half << 2)));
-            const i16x4 hi = lds_read_tr(vrow1 + (((ch ^ sw1) << 3) | (half << 2)));
-            const bf16x8 va =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[kc2], O[db], 0, 0, 0);
+            const i16x4 lo = lds_read_tr(vp0 + db * 32);
+            const i16x4 hi = lds_read_tr(vp0 + 4 * VR + db * 32);
+            va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], P[kc2], O[db], 0, 0, 0);
         }
       }
       if (t + 1 < ntiles) store_tile((t + 1) & 1);
@@ -280,22 +305,35 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
     }
 
     // Epilogue: O^T holds dims db*32 + 8*(v/4) + 4*hh + v%4 of query row `row`.
-    const float lt = l + __shfl_xor(l, 32);
-    if (row_ok) {
-      const float inv = 1.0f / lt;
-      float* op = a.slot_o + ((size_t)slot * a.M + row) * D;
+    // Normalise, round to bf16 and stage this wave's 32 rows in LDS (16-byte
+    // units XOR-swizzled by row), then write them out as whole contiguous rows.
+    const float lt = half_sum(l);
+    const float inv = 1.0f / lt;
+    unsigned short* stg = lds + wave * 32 * D;
+    if (computes) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 val;
-          val[0] = O[db][4 * g4 + 0] * inv;
-          val[1] = O[db][4 * g4 + 1] * inv;
-          val[2] = O[db][4 * g4 + 2] * inv;
-          val[3] = O[db][4 * g4 + 3] * inv;
-          *(f32x4*)(op + db * 32 + 8 * g4 + 4 * hh) = val;
-        }
-      if (hh == 0) a.slot_lse2[(size_t)slot * a.M + row] = m + fast_log2(lt);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hh;
+        u32x2 pk;
+        pk[0] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 0] * inv) |
+                ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 1] * inv) << 16);
+        pk[1] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 2] * inv) |
+                ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 3] * inv) << 16);
+        *(u32x2*)(stg + l32 * D + ((((d >> 3) ^ (l32 & (DCH - 1)))) << 3) + (d & 7)) = pk;
+      }
+    }
+    if (row_ok && hh == 0) a.slot_lse2[(size_t)slot * a.M + row] = m + fast_log2(lt);
+    __syncthreads();
+    const int wrow0 = blockIdx.y * a.rows_per_group + wave * 32;  // first row of this wave
+#pragma unroll
+    for (int i = 0; i < (computes ? 32 * DCH / 64 : 0); ++i) {
+      const int u = i * 64 + lane;
+      const int rr = u / DCH, c = u % DCH;
+      const u32x4 val = *(const u32x4*)(stg + rr * D + ((c ^ (rr & (DCH - 1))) << 3));
+      if (wrow0 + rr < row_limit)
+        *(u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8) = val;
     }
     if (has_tree && g == 0 && blockIdx.y == 0 && tid == 0) {
       a.err_b[b] = bad_s;
@@ -305,7 +343,7 @@ __global__ void __launch_bounds__(64 * WQ) prefix_mfma_kernel(PrefixArgs a) {
     x = piece_end;
     if (x >= x_end) break;
     if (!walk_next(&sw, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles)) break;
-    __syncthreads();  // par_s / anc_s / bad_s of this piece are no longer read
+    __syncthreads();  // staging area, par_s / anc_s / bad_s of this piece are no longer read
   }
 }
 
@@ -328,10 +366,10 @@ KernelFn pick_d(int wq) {
 
 KernelFn pick(int D, int wq, int qb) {
   if (qb != 1) return nullptr;
-  if (D == 128) return pick_d<128>(wq);
-  if (D == 64) return pick_d<64>(wq);
-  return nullptr;
+  return D == 128 ? pick_d<128>(wq) : D == 64 ? pick_d<64>(wq) : nullptr;
 }
+
+int threads_of(int waves) { return waves <= 4 ? 256 : 512; }
 
 }  // namespace
 
@@ -341,7 +379,8 @@ int prefix_mfma_occupancy(int D, int waves, int qb) {
   KernelFn k = pick(D, waves, qb);
   if (!k) return 0;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), 64 * waves, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k),
+                                                   threads_of(waves), 0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;
@@ -359,7 +398,7 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
   a.vt = static_cast<const unsigned short*>(in.v_tree);
   a.parent = in.parent;
   a.prefix_len = in.prefix_len;
-  a.slot_o = slots.o;
+  a.slot_o = static_cast<unsigned short*>(slots.o);
   a.slot_lse2 = slots.lse2;
   a.err_b = err_b;
   a.status = status;
@@ -374,7 +413,7 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
   a.rows_per_group = pl.rows_per_group;
   a.tree_tiles = in.k_tree ? 1 : 0;
   a.scale_log2 = d.scale_log2;
-  hipLaunchKernelGGL(k, dim3(pl.nwg, pl.row_groups), dim3(64 * pl.waves), 0, s, a);
+  hipLaunchKernelGGL(k, dim3(pl.nwg, pl.row_groups), dim3(threads_of(pl.waves)), 0, s, a);
   return hipGetLastError();
 }
 

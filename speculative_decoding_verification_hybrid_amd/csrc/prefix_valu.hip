@@ -25,7 +25,7 @@ struct ValuArgs {
   const void* vt;
   const int* parent;
   const int* prefix_len;
-  float* slot_o;
+  float* slot_o;  // float partials
   float* slot_lse2;
   int* err_b;
   int* status;
@@ -205,7 +205,7 @@ hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const Prefi
   a.vt = in.v_tree;
   a.parent = in.parent;
   a.prefix_len = in.prefix_len;
-  a.slot_o = slots.o;
+  a.slot_o = static_cast<float*>(slots.o);
   a.slot_lse2 = slots.lse2;
   a.err_b = err_b;
   a.status = status;
