@@ -1,19 +1,28 @@
 """Benchmark: tree-verification attention at the Llama-3.1-8B layer shape.
 
-One step = one hta_verify_attn call (tree kernel + split-KV prefix kernel +
-merge) over one batch of synthetic inputs: 32 query / 8 KV heads, head_dim
-128, a 32768-token bf16 KV prefix and a 64-node draft tree. Inputs are
-resident in HBM before the timed region; the KV cache is rotated over
-enough replicas (>= 512 MB) that the 256 MB Infinity Cache cannot hold the
-next step's KV, so every step streams its KV from HBM.
+One step = one hta_verify_attn call (split-KV kernel with the tree part fused
+in, then the LSE merge) over one batch of synthetic inputs: 32 query / 8 KV
+heads, head_dim 128, a 32768-token bf16 KV prefix and a 64-node draft tree.
+Inputs are resident in HBM before the timed region; the KV cache is rotated
+over enough replicas (>= 512 MB) that the 256 MB Infinity Cache cannot hold
+the next step's KV, so every step streams its KV from HBM.
 
-Prints one JSON line. ``value`` is the layer's achieved HBM bandwidth on
-its algorithmic bytes (valid KV read once + q, tree K/V, out, lse, tree
-shape); the per-layer latency, verified tokens/s, the split-KV kernel's
-roofline (timed alone over the same rotation) and the fp64 CPU oracle's
-throughput on a bounded sample of the same workload are reported beside it.
+The K timed steps are captured once into a HIP graph and replayed once
+between two events on the replay stream, so the figure is GPU time, not the
+cost of launching from Python. The warm-up is W eager steps plus one untimed
+replay of the graph. The graph's outputs are checked bit for bit against an
+eager step on the same inputs.
+
+Prints one JSON line. ``value`` is the layer's achieved HBM bandwidth on its
+algorithmic bytes (valid KV read once + q, tree K/V, out, lse, tree shape);
+beside it: the per-layer latency, verified tokens/s, the split-KV kernel's
+roofline (its K launches captured and timed the same way, alone) and the fp64
+CPU oracle's throughput on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --copy-calibration   (adds 8 launches of a plain elementwise
+           kernel that reads 256 MiB and writes 256 MiB before the timed region:
+           the reference dispatches that HBM byte counters are scaled by)
 """
 
 import argparse
@@ -46,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run 8 copy-like 256 MiB elementwise kernels before timing")
     return ap.parse_args()
 
 
@@ -133,34 +144,58 @@ def main():
                           kv_capacity=w.Lcap, dtype="bf16", softmax_scale=w.scale)
     h = hta.hta_create(cfg)
     plan = hta.hta_get_plan(h)
-    stream = torch.cuda.current_stream()
 
-    def step(i):
-        hta.hta_verify_attn(h, q, kcs[i % R], vcs[i % R], kt, vt, parent, plen, out, lse, stream)
+    def step(i, s):
+        hta.hta_verify_attn(h, q, kcs[i % R], vcs[i % R], kt, vt, parent, plen, out, lse, s)
 
-    def prefix_only(i):
-        hta.hta_prefix_partials(h, q, kcs[i % R], vcs[i % R], plen, stream)
+    def prefix_only(i, s):
+        hta.hta_prefix_partials(h, q, kcs[i % R], vcs[i % R], plen, s)
 
     def timed(fn, steps, warmup):
+        """Average GPU time of one fn step: `steps` steps captured in one graph,
+        replayed once between two events on the stream the graph runs on."""
+        s = torch.cuda.current_stream()
         for i in range(warmup):
-            fn(i)
+            fn(i, s)
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record(stream)
-        for i in range(steps):
-            fn(warmup + i)
-            ev[i + 1].record(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            for i in range(steps):
+                fn(warmup + i, cs)
+        g.replay()  # untimed: uploads the graph
         torch.cuda.synchronize()
-        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-        total = ev[0].elapsed_time(ev[steps])
-        return total / steps, per
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, g
 
-    # whole layer
-    ms, per = timed(step, args.steps, args.warmup)
+    if args.copy_calibration:
+        src = torch.empty(128 << 20, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            torch.bitwise_not(src, out=dst)  # one elementwise kernel: 256 MiB in, 256 MiB out
+        torch.cuda.synchronize()
+        del src, dst
+
+    # eager reference step, then the whole layer as a graph of K steps
+    step(0, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    out_eager, lse_eager = out.clone(), lse.clone()
+    out.zero_()
+    lse.zero_()
+    ms, g_layer = timed(step, args.steps, args.warmup)
     status = hta.hta_get_status(h)
-    ok = bool(torch.isfinite(out.float()).all().item()) and status == 0
-    # the split-KV prefix kernel alone, same rotation
-    pms, pper = timed(prefix_only, args.steps, args.warmup)
+    same = bool(torch.equal(out, out_eager)) and bool(torch.equal(lse, lse_eager))
+    ok = same and bool(torch.isfinite(out.float()).all().item()) and status == 0
+    del g_layer
+    # the split-KV kernel alone, same rotation
+    pms, g_prefix = timed(prefix_only, args.steps, args.warmup)
+    del g_prefix
+    torch.cuda.synchronize()
     hta.hta_destroy(h)
 
     layer_us = ms * 1e3
@@ -184,10 +219,9 @@ def main():
                    "head_dim": w.D, "prefix_len": int(w.prefix_len[0]), "tree_nodes": w.T,
                    "kv_replicas": R},
         "layer_us": round(layer_us, 3),
-        "layer_us_p10_p50_p90": [round(float(np.percentile(per, p)) * 1e3, 3) for p in (10, 50, 90)],
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "tokens_per_s_verified": round(w.B * w.T / (ms * 1e-3), 1),
-        "outputs_finite_and_status_ok": ok,
+        "outputs_match_eager_finite_status_ok": ok,
         "plan": {k: plan[k] for k in ("path", "num_workgroups", "waves_per_workgroup",
                                       "qblocks_per_wave", "row_groups", "compute_units")},
         "roofline": {

@@ -60,6 +60,8 @@ int validate(const hta_config_t* c) {
 void plan_rows(const hta::Dims& d, int path, hta::PrefixLaunch* pl) {
   pl->path = path;
   if (path == HTA_PATH_MFMA) {
+    // one wave per 32-row q-block, up to 8 per workgroup; more rows go to
+    // further row groups (grid.y)
     const int nqb = (d.M + 31) / 32;
     const int rg = (nqb + 7) / 8;
     const int per = (nqb + rg - 1) / rg;

@@ -29,7 +29,7 @@ struct PrefixLaunch {
   int nwg;            // workgroups per row group
   int row_groups;     // grid.y
   int rows_per_group; // multiple of 32 (MFMA) or of 16 (VALU)
-  int waves;          // MFMA: WQ
+  int waves;          // MFMA: waves that compute
   int qb;             // MFMA: q-blocks per wave
 };
 

@@ -13,11 +13,26 @@
 // ancestor mask built in LDS from parent[] -- the same online softmax then
 // covers both parts, and the merge combines the pieces.
 //
-// Per workgroup: WQ waves, each owning one block of 32 query rows (two waves
-// per SIMD at WQ = 8, so one wave's softmax overlaps the other's MFMA). Per
-// tile, all waves share one copy of K and V in LDS, both row-major. K rows are
-// padded by 16 bytes and V rows by 64 bytes, which makes the reads below free
-// of bank conflicts while every read is a base register plus an immediate:
+// Memory pipeline: K and V tiles go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no staging registers), through 4 LDS stages, so up
+// to 3 tiles (96 KB at D = 128) are in flight per workgroup while one is
+// consumed. Each wave waits for its own copies (vmcnt), then all waves meet at
+// one barrier per tile, after which the stage of the tile just finished is
+// refilled. The copies are issued from inline assembly, so the compiler's wait
+// insertion never sees them (it would otherwise drain the whole copy queue
+// before LDS reads it cannot prove disjoint from a copy in flight); every wait
+// on them is explicit, and the only compiler-issued vector loads (the Q
+// fragments) complete before the first copy of a piece.
+//
+// One copy instruction moves 1 KB: 4 (D = 128) or 8 (D = 64) whole rows of K
+// or V, read coalesced from HBM, with the lanes' 16-byte chunks permuted on
+// the way into LDS. K rows keep their 16-byte chunks XOR-swizzled by row; V is
+// stored as 128-byte blocks of 4 tokens x 16 dims, which is exactly what one
+// 16-lane group of a transposed read consumes.
+//
+// Compute: WQ waves (two per SIMD at WQ = 8), each owning one block of 32
+// query rows; the first wave of each SIMD runs at higher priority, so the pair
+// drifts into alternating MFMA and softmax phases.
 //   * scores are computed transposed, S^T = K . Q^T: each lane holds one
 //     query row (a column of the MFMA result) and 16 tokens, so the row max
 //     needs one cross-half exchange and the running (m, l) live in lanes;
@@ -29,10 +44,15 @@
 //     lane i receives element i%4 of the 8-byte chunks read by lanes
 //     4j + i/4 (j = 0..3), so lanes that read 4 dims of 4 consecutive tokens
 //     hand each lane 4 consecutive tokens of one dim.
+// LDS reads run ahead of their use: the V fragments of a 32-token sub-tile
+// are read while its score MFMAs run, and the K fragments of the next
+// sub-tile while the softmax runs.
 // Online softmax runs in the log2 domain with a lazily updated maximum: the
-// stored max only moves when a tile's max exceeds it by more than 8 (so
+// stored max only moves when a sub-tile's max exceeds it by more than 8 (so
 // exp2 stays below 256), which is exact because the same stale max is used
 // for both the sum and the output.
+#include <type_traits>
+
 #include "common.h"
 #include "hta_internal.h"
 
@@ -40,6 +60,7 @@ namespace hta {
 namespace {
 
 constexpr int NK = kTileTokens;
+constexpr int NSTAGE = 4;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -60,15 +81,22 @@ struct PrefixArgs {
   float scale_log2;
 };
 
-// LDS row strides (bf16 elements). K: 16-byte pad, so the 16 rows of a K
-// fragment read start 4 banks apart. V: 64-byte pad, so the 4 rows x 4 chunks
-// of a transposed V read cover all 64 banks once (D = 128: rows 16 banks
-// apart; D = 64: rows 48 banks apart).
+// XOR swizzle of the 16-byte chunks of K row r. D = 128: a row spans all 64
+// banks and the swizzle is a bijection of r's low 4 bits, so the 16 rows of a
+// K fragment read hit 16 different chunks. D = 64: two rows share the banks,
+// and the same holds per half.
 template <int D>
-struct Rows {
-  static constexpr int K = D + 8;
-  static constexpr int V = D + 32;
-};
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// MFMA row -> token within a 32-token sub-tile: swap bits 2 and 3.
+__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+__device__ __forceinline__ i16x4 lds_read_tr(const unsigned short* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
 
 // Cross-half (lane l <-> l ^ 32) max and sum in VALU: the two results of the
 // lane swap are this lane's value and its partner's, in some order.
@@ -81,32 +109,62 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// MFMA row -> token within a 32-token sub-tile: swap bits 2 and 3.
-__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maximum).
+template <int N>
+constexpr int vmcnt_only() {
+  return (N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8);
+}
+constexpr int kLgkmZero = 15 | (7 << 4) | (3 << 14);  // lgkmcnt(0) only
 
-__device__ __forceinline__ i16x4 lds_read_tr(const unsigned short* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+// Workgroup barrier that orders LDS accesses only in the compiler: the
+// hardware waits for the tile copies are the explicit ones before it (a memory
+// fence here would drain every copy in flight).
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// Threads per workgroup: the WQ compute waves plus loader-only waves up to 4
-// (WQ <= 4) or 8, so no wave stages more than 8 chunks of a tile.
+// One 16-byte-per-lane copy from global memory into LDS: lane i's 16 bytes
+// land at LDS byte address lds_base + 16 i. lds_base must be wave-uniform (it
+// goes through M0, which needs one wait state before the copy). The "memory"
+// clobber keeps the compiler from moving LDS accesses across the copy.
+__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const unsigned short* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned short*)p;
+}
+
+// Threads per workgroup: the WQ compute waves plus copy-only waves up to 4
+// (WQ <= 4) or 8.
 template <int WQ>
 constexpr int threads_for() { return WQ <= 4 ? 256 : 512; }
 
 template <int D, int WQ>
 __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixArgs a) {
-  constexpr int NT = threads_for<WQ>();
+  constexpr int NWAVE = threads_for<WQ>() / 64;
   constexpr int KC = D / 16;          // k-chunks of K.Q^T
   constexpr int DB = D / 32;          // 32-dim blocks of O
   constexpr int DCH = D / 8;          // 16-byte chunks per row
-  constexpr int KR = Rows<D>::K, VR = Rows<D>::V;
-  constexpr int KT = NK * KR;         // bf16 elements of one K tile
-  constexpr int STAGE = KT + NK * VR; // K tile + V tile
-  constexpr int CH = 2 * NK * DCH;    // 16-byte chunks of K + V per tile
-  constexpr int NL = (CH + NT - 1) / NT;
-  static_assert(2 * STAGE >= WQ * 32 * D, "epilogue staging reuses the tile buffers");
+  constexpr int DG = D / 16;          // 16-dim groups (V blocks per 4 tokens)
+  constexpr int TILE = NK * D;        // bf16 elements of one K (or V) tile
+  constexpr int STAGE = 2 * TILE;     // K tile, then V tile
+  constexpr int RPB = 64 / DCH;       // rows per 1 KB copy block
+  constexpr int NBLK = NK / RPB;      // copy blocks per K (or V) tile
+  constexpr int NBH = NBLK / NWAVE;   // K (and V) copy instructions per wave per tile
+  constexpr int GRP = 2 * NBH;        // copy instructions per wave per tile
+  constexpr int SROW = D + 8;         // epilogue staging row (16-byte aligned rows)
+  static_assert(NBLK % NWAVE == 0, "copy blocks split evenly over the waves");
+  static_assert(NSTAGE * STAGE >= NWAVE * 32 * SROW, "epilogue staging fits in the tile buffers");
+  static_assert(3 * GRP < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) unsigned short lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned short lds[NSTAGE * STAGE];
   __shared__ int par_s[64];
   __shared__ unsigned long long anc_s[64];
   __shared__ int bad_s;
@@ -118,6 +176,7 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
   const int l32 = lane & 31;
   const int grp = lane >> 4;  // 16-lane group (transposed V reads)
   const int gl = lane & 15;
+  if (NWAVE == 8 && wave < 4) __builtin_amdgcn_s_setprio(2);
 
   const int w = xcd_remap(blockIdx.x, a.nwg);
   const unsigned TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles);
@@ -128,11 +187,31 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
   SegmentWalk sw;
   if (!walk_start(&sw, x, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles)) return;
 
-  const bool computes = wave < WQ;  // loader-only waves stage tiles and hit the barriers
+  const bool computes = wave < WQ;  // copy-only waves issue copies and meet the barriers
   const int row = blockIdx.y * a.rows_per_group + wave * 32 + l32;  // this lane's query row
   const int row_limit = min(a.M, (int)(blockIdx.y + 1) * a.rows_per_group);
   const bool row_ok = computes && row < row_limit;
   const int node = row_ok ? row % a.T : 0;
+
+  // Lane-constant LDS offsets (elements, within a stage). K: the fragments of
+  // this lane's row; the swizzle depends only on the row's low 4 bits, which
+  // are the same in both 32-token sub-tiles.
+  int koff[KC];
+  {
+    const int kr = kperm(l32);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) koff[c] = kr * D + (((2 * c + hh) ^ swz<D>(kr)) << 3);
+  }
+  // V block (4 tokens x 16 dims, 64 elements) of tokens 4u.., dims 16g..: (u * DG + g) * 64.
+  // A transposed read of tokens 32st + 16kc + 8hh + 4rr, dims 32db + 16(grp&1) + 0..15
+  // reads block ((8st + 4kc + 2hh + rr) * DG + 2db + (grp&1)), lane gl at 4 gl.
+  const int voff = TILE + (2 * hh * DG + (grp & 1)) * 64 + 4 * gl;
+  // This lane's part of a 1 KB copy block. K: row within the block and logical
+  // chunk. V: token within the block and dims (the V block layout above).
+  const int cp_row = lane / DCH;
+  const int cp_kc = lane % DCH;
+  const int cp_vt = ((lane >> 3) / DG) * 4 + ((lane & 7) >> 1);
+  const int cp_vd = ((lane >> 3) % DG) * 16 + (lane & 1) * 8;
 
   while (true) {
     const int b = sw.b, g = sw.g;
@@ -150,6 +229,7 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
     const size_t kt_off = (size_t)(b * a.Hkv + g) * a.T * D;
     const unsigned short* qp = a.q + (size_t)(b * a.Hq + g * a.G) * a.T * D;
 
+    unsigned long long anc_row = 0ull;
     if (has_tree) {
       if (tid == 0) bad_s = 0;
       if (tid < a.T) par_s[tid] = a.parent[(size_t)b * a.T + tid];
@@ -159,51 +239,58 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
         anc_s[tid] = ancestor_word(par_s, tid, &ok);
         if (!ok) bad_s = 1;
       }
-      // read after the barrier that follows the first tile store below
+      __syncthreads();
+      anc_row = anc_s[node];
     }
 
     // Q^T fragments (B operand of S^T = K.Q^T): row `row`, dims 16c + 8hh .. +7.
     bf16x8 qf[KC];
+    {
+      const unsigned short* qr = qp + (size_t)(row_ok ? row : 0) * D + 8 * hh;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (row_ok) r = *(const u32x4*)(qp + (size_t)row * D + 16 * c + 8 * hh);
-      qf[c] = __builtin_bit_cast(bf16x8, r);
+      for (int c = 0; c < KC; ++c) {
+        u32x4 r = *(const u32x4*)(qr + 16 * c);
+        if (!row_ok) r = u32x4{0u, 0u, 0u, 0u};
+        qf[c] = __builtin_bit_cast(bf16x8, r);
+      }
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());  // Q is in registers before any copy is queued
 
-    // Stage a tile through registers: chunk idx < NK*DCH is K, the rest V.
-    // Rows past the tile's valid tokens are zero (V of a masked token must be 0).
-    u32x4 reg[NL];
-    auto load_tile = [&](int ti) {
+    // Queue the copies of tile t of the piece into stage t % NSTAGE: this
+    // wave's NBH blocks of K and NBH blocks of V. Rows past the tile's valid
+    // tokens repeat its last valid row, so every value read is finite and in
+    // bounds; their scores are masked to -inf.
+    auto copy_tile = [&](int t) __attribute__((always_inline)) {
+      const int ti = tile0 + t;
       const bool tree = ti >= n_prefix;
       const unsigned short* ks = tree ? a.kt + kt_off : kp + (size_t)ti * NK * D;
       const unsigned short* vs = tree ? a.vt + kt_off : vp + (size_t)ti * NK * D;
-      const int nv = tree ? a.T : min(NK, L - ti * NK);
+      const int last = (tree ? a.T : min(NK, L - ti * NK)) - 1;
+      unsigned short* dst = lds + (t % NSTAGE) * STAGE;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int idx = tid + i * NT;
-        if (CH % NT == 0 || idx < CH) {
-          const int is_v = idx >= NK * DCH;
-          const int e = idx - is_v * NK * DCH;
-          const int r = e / DCH, c = e % DCH;
-          u32x4 val = {0u, 0u, 0u, 0u};
-          if (r < nv) val = *(const u32x4*)((is_v ? vs : ks) + (size_t)r * D + c * 8);
-          reg[i] = val;
-        }
+      for (int i = 0; i < NBH; ++i) {
+        const int r0 = (wave + i * NWAVE) * RPB;  // first row of the block
+        const int r = r0 + cp_row;
+        copy16_to_lds(ks + (size_t)min(r, last) * D + ((cp_kc ^ swz<D>(r)) << 3),
+                      __builtin_amdgcn_readfirstlane(lds_addr(dst + r0 * D)));
+      }
+#pragma unroll
+      for (int i = 0; i < NBH; ++i) {
+        const int r0 = (wave + i * NWAVE) * RPB;
+        copy16_to_lds(vs + (size_t)min(r0 + cp_vt, last) * D + cp_vd,
+                      __builtin_amdgcn_readfirstlane(lds_addr(dst + TILE + r0 * D)));
       }
     };
-    auto store_tile = [&](int stage) {
-      unsigned short* base = lds + stage * STAGE;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int idx = tid + i * NT;
-        if (CH % NT == 0 || idx < CH) {
-          const int is_v = idx >= NK * DCH;
-          const int e = idx - is_v * NK * DCH;
-          const int r = e / DCH, c = e % DCH;
-          *(u32x4*)(base + (is_v ? KT + r * VR : r * KR) + c * 8) = reg[i];
-        }
-      }
+    // Wait until at most n tiles' copies of this wave are still in flight.
+    auto wait_tiles = [&](int n) __attribute__((always_inline)) {
+      if (n >= 3)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<3 * GRP>());
+      else if (n == 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<2 * GRP>());
+      else if (n == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<GRP>());
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
     };
 
     f32x16 O[DB];
@@ -212,37 +299,47 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
 #pragma unroll
       for (int v = 0; v < 16; ++v) O[db][v] = 0.f;
     float m = -__builtin_inff(), l = 0.f;
-    unsigned long long anc_row = 0ull;
 
-    load_tile(tile0);
-    store_tile(0);
-    __syncthreads();
-    if (has_tree) anc_row = anc_s[node];
+    bf16x8 ka[KC];
+    auto load_k = [&](const unsigned short* kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) ka[c] = *(const bf16x8*)(kb + koff[c]);
+    };
+
+    // Every stage starts filled: tile t goes to stage t % NSTAGE, and the stage
+    // of tile t is refilled (with tile t + NSTAGE) once tile t is consumed.
+    for (int t = 0; t < min(ntiles, NSTAGE); ++t) copy_tile(t);
+    wait_tiles(min(ntiles, NSTAGE) - 1);
+    tile_barrier();
+    if (computes) load_k(lds);
 
     for (int t = 0; t < ntiles; ++t) {
+      const unsigned short* Ks = lds + (t % NSTAGE) * STAGE;
       const int ti = tile0 + t;
-      if (t + 1 < ntiles) load_tile(ti + 1);
-      const unsigned short* Ks = lds + (t & 1) * STAGE;
-      const unsigned short* Vs = Ks + KT;
       const bool tree = ti >= n_prefix;
       const int nvalid = tree ? a.T : min(NK, L - ti * NK);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (!computes || st * 32 >= nvalid) break;
-        // S^T = K . Q^T for 32 tokens: fetch all 8 K fragments, then the MFMA chain.
-        const unsigned short* krow = Ks + (st * 32 + kperm(l32)) * KR + 8 * hh;
-        bf16x8 ka[KC];
-#pragma unroll
-        for (int c = 0; c < KC; ++c) ka[c] = *(const bf16x8*)(krow + 16 * c);
+        // S^T = K . Q^T for 32 tokens (K fragments already in registers).
         f32x16 S;
 #pragma unroll
         for (int v = 0; v < 16; ++v) S[v] = 0.f;
 #pragma unroll
         for (int c = 0; c < KC; ++c) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], S, 0, 0, 0);
-        // keep the K reads ahead of the chain (the scheduler would otherwise sink
-        // each read next to its MFMA and pay the LDS latency 8 times)
-        __builtin_amdgcn_sched_group_barrier(0x100, KC, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, KC, 0);  // MFMAs
+        // V^T fragments of this sub-tile: tokens 16kc + 8hh + 0..7, dims 32db + lane%32.
+        bf16x8 va[2][DB];
+        {
+          const unsigned short* vb = Ks + voff + 8 * st * DG * 64;
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const i16x4 lo = lds_read_tr(vb + (4 * kc * DG + 2 * db) * 64);
+              const i16x4 hi = lds_read_tr(vb + ((4 * kc + 1) * DG + 2 * db) * 64);
+              va[kc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
         // S[v] scores token st*32 + 16*(v/8) + 8*hh + v%8 of the tile. On the
         // tree tile and on a ragged last tile, bit v of `vis` says whether that
         // token is seen; hidden scores get -inf added (no compares, no masks).
@@ -256,8 +353,7 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
             vis = ((1u << n0) - 1u) | (((1u << n1) - 1u) << 8);
           }
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            S[v] += __uint_as_float((((vis >> v) & 1u) - 1u) & 0xff800000u);
+          for (int v = 0; v < 16; ++v) S[v] += __uint_as_float((((vis >> v) & 1u) - 1u) & 0xff800000u);
         }
         float mx0 = fmaxf(fmaxf(S[0], S[1]), S[2]), mx1 = fmaxf(fmaxf(S[3], S[4]), S[5]);
         float mx2 = fmaxf(fmaxf(S[6], S[7]), S[8]), mx3 = fmaxf(fmaxf(S[9], S[10]), S[11]);
@@ -272,6 +368,8 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
 #pragma unroll
           for (int db = 0; db < DB; ++db) O[db] *= alpha;
         }
+        // Probabilities: the row sum adds them in fp32 (four partial sums), the
+        // P.V product takes them rounded to bf16.
         const float nm = m == -__builtin_inff() ? 0.f : -m;
         bf16x8 P[2];
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
@@ -282,47 +380,48 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
           P[v >> 3][v & 7] = (__bf16)p;
         }
         l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        // K fragments of the next sub-tile of this tile, read while P.V runs.
+        if (st == 0 && nvalid > 32) load_k(Ks + 32 * D);
         // O^T += V^T . P^T over the two 16-token k-chunks of this sub-tile.
 #pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
-          // rows vr and vr + 4 of the tile; dims of this lane's 4-dim group
-          const int vr = st * 32 + 16 * kc2 + 8 * hh + (gl >> 2);
-          const unsigned short* vp0 = Vs + vr * VR + 16 * (grp & 1) + 4 * (gl & 3);
-          bf16x8 va[DB];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const i16x4 lo = lds_read_tr(vp0 + db * 32);
-            const i16x4 hi = lds_read_tr(vp0 + 4 * VR + db * 32);
-            va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], P[kc2], O[db], 0, 0, 0);
-        }
+            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kc][db], P[kc], O[db], 0, 0, 0);
       }
-      if (t + 1 < ntiles) store_tile((t + 1) & 1);
-      __syncthreads();
+      if (t + 1 < ntiles) {
+        // Tile t+1 has landed for every wave (at most tiles t+2, t+3 still in
+        // flight: tiles up to t+3 have been queued) and every wave's reads of
+        // tile t are done: its stage takes tile t+4. Then the K fragments of
+        // tile t+1.
+        __builtin_amdgcn_s_waitcnt(kLgkmZero);
+        wait_tiles(min(ntiles - 2 - t, 2));
+        tile_barrier();
+        if (t + NSTAGE < ntiles) copy_tile(t + NSTAGE);
+        if (computes) load_k(lds + ((t + 1) % NSTAGE) * STAGE);
+      }
     }
+    __syncthreads();  // no wave reads the tile buffers any more (all copies landed before the last barrier)
 
     // Epilogue: O^T holds dims db*32 + 8*(v/4) + 4*hh + v%4 of query row `row`.
-    // Normalise, round to bf16 and stage this wave's 32 rows in LDS (16-byte
-    // units XOR-swizzled by row), then write them out as whole contiguous rows.
+    // Normalise, round to bf16 and stage this wave's 32 rows in LDS (rows
+    // padded by 16 bytes), then write them out as whole contiguous rows.
     const float lt = half_sum(l);
     const float inv = 1.0f / lt;
-    unsigned short* stg = lds + wave * 32 * D;
+    unsigned short* stg = lds + wave * 32 * SROW;
     if (computes) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hh;
-        u32x2 pk;
-        pk[0] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 0] * inv) |
-                ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 1] * inv) << 16);
-        pk[1] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 2] * inv) |
-                ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 3] * inv) << 16);
-        *(u32x2*)(stg + l32 * D + ((((d >> 3) ^ (l32 & (DCH - 1)))) << 3) + (d & 7)) = pk;
-      }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + 8 * g4 + 4 * hh;
+          u32x2 pk;
+          pk[0] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 0] * inv) |
+                  ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 1] * inv) << 16);
+          pk[1] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 2] * inv) |
+                  ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 3] * inv) << 16);
+          *(u32x2*)(stg + l32 * SROW + d) = pk;
+        }
     }
     if (row_ok && hh == 0) a.slot_lse2[(size_t)slot * a.M + row] = m + fast_log2(lt);
     __syncthreads();
@@ -331,9 +430,8 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
     for (int i = 0; i < (computes ? 32 * DCH / 64 : 0); ++i) {
       const int u = i * 64 + lane;
       const int rr = u / DCH, c = u % DCH;
-      const u32x4 val = *(const u32x4*)(stg + rr * D + ((c ^ (rr & (DCH - 1))) << 3));
-      if (wrow0 + rr < row_limit)
-        *(u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8) = val;
+      const u32x4 val = *(const u32x4*)(stg + rr * SROW + c * 8);
+      if (wrow0 + rr < row_limit) *(u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8) = val;
     }
     if (has_tree && g == 0 && blockIdx.y == 0 && tid == 0) {
       a.err_b[b] = bad_s;
@@ -364,9 +462,9 @@ KernelFn pick_d(int wq) {
   }
 }
 
-KernelFn pick(int D, int wq, int qb) {
+KernelFn pick(int D, int waves, int qb) {
   if (qb != 1) return nullptr;
-  return D == 128 ? pick_d<128>(wq) : D == 64 ? pick_d<64>(wq) : nullptr;
+  return D == 128 ? pick_d<128>(waves) : D == 64 ? pick_d<64>(waves) : nullptr;
 }
 
 int threads_of(int waves) { return waves <= 4 ? 256 : 512; }
@@ -379,8 +477,7 @@ int prefix_mfma_occupancy(int D, int waves, int qb) {
   KernelFn k = pick(D, waves, qb);
   if (!k) return 0;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k),
-                                                   threads_of(waves), 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), threads_of(waves), 0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;
