@@ -50,7 +50,9 @@
 // Online softmax runs in the log2 domain with a lazily updated maximum: the
 // stored max only moves when a sub-tile's max exceeds it by more than 8 (so
 // exp2 stays below 256), which is exact because the same stale max is used
-// for both the sum and the output.
+// for both the sum and the output. The row max itself is only computed when
+// the probabilities against the stored max sum to more than 256 (the sum
+// bounds every term), which after the first sub-tile is rare.
 #include <type_traits>
 
 #include "common.h"
@@ -126,14 +128,16 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One 16-byte-per-lane copy from global memory into LDS: lane i's 16 bytes
-// land at LDS byte address lds_base + 16 i. lds_base must be wave-uniform (it
-// goes through M0, which needs one wait state before the copy). The "memory"
-// clobber keeps the compiler from moving LDS accesses across the copy.
-__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// One 16-byte-per-lane copy from global memory into LDS: lane i reads the 16
+// bytes at base + off (base wave-uniform, in SGPRs; off a 32-bit per-lane byte
+// offset) and they land at LDS byte address lds_base + 16 i. lds_base must be
+// wave-uniform (it goes through M0, which needs one wait state before the
+// copy). The "memory" clobber keeps the compiler from moving LDS accesses
+// across the copy.
+__device__ __forceinline__ void copy16_to_lds(const void* base, unsigned off, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds_base)
+               : "v"(off), "s"(base), "s"(lds_base)
                : "memory", "m0");
 }
 
@@ -171,7 +175,7 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int hh = lane >> 5;
   const int l32 = lane & 31;
   const int grp = lane >> 4;  // 16-lane group (transposed V reads)
@@ -269,16 +273,15 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
       unsigned short* dst = lds + (t % NSTAGE) * STAGE;
 #pragma unroll
       for (int i = 0; i < NBH; ++i) {
-        const int r0 = (wave + i * NWAVE) * RPB;  // first row of the block
+        const int r0 = (wave + i * NWAVE) * RPB;  // first row of the block (wave-uniform)
         const int r = r0 + cp_row;
-        copy16_to_lds(ks + (size_t)min(r, last) * D + ((cp_kc ^ swz<D>(r)) << 3),
-                      __builtin_amdgcn_readfirstlane(lds_addr(dst + r0 * D)));
+        copy16_to_lds(ks, (unsigned)(min(r, last) * D + ((cp_kc ^ swz<D>(r)) << 3)) * 2u,
+                      lds_addr(dst + r0 * D));
       }
 #pragma unroll
       for (int i = 0; i < NBH; ++i) {
         const int r0 = (wave + i * NWAVE) * RPB;
-        copy16_to_lds(vs + (size_t)min(r0 + cp_vt, last) * D + cp_vd,
-                      __builtin_amdgcn_readfirstlane(lds_addr(dst + TILE + r0 * D)));
+        copy16_to_lds(vs, (unsigned)(min(r0 + cp_vt, last) * D + cp_vd) * 2u, lds_addr(dst + TILE + r0 * D));
       }
     };
     // Wait until at most n tiles' copies of this wave are still in flight.
@@ -355,31 +358,46 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
 #pragma unroll
           for (int v = 0; v < 16; ++v) S[v] += __uint_as_float((((vis >> v) & 1u) - 1u) & 0xff800000u);
         }
-        float mx0 = fmaxf(fmaxf(S[0], S[1]), S[2]), mx1 = fmaxf(fmaxf(S[3], S[4]), S[5]);
-        float mx2 = fmaxf(fmaxf(S[6], S[7]), S[8]), mx3 = fmaxf(fmaxf(S[9], S[10]), S[11]);
-        float mx4 = fmaxf(fmaxf(S[12], S[13]), S[14]);
-        float mx = fmaxf(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3)), fmaxf(mx4, S[15]));
-        mx = half_max(mx) * a.scale_log2;
-        if (__any(mx > m + 8.0f)) {
-          const float mn = fmaxf(m, mx);
-          const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mn);
-          m = mn;
-          l *= alpha;
+        // Probabilities against the stored max m; the row sum adds them in fp32
+        // (four partial sums), the P.V product takes them rounded to bf16. The
+        // sum bounds every term, so if it stays <= 256 so does each
+        // p = 2^(s - m) and m can stay. Otherwise (and always while m is still
+        // -inf) take the exact row max over both half-rows; if it exceeds m by
+        // more than 8, raise m, rescale l and O, and recompute.
+        float pr[16];
+        auto probs = [&]() __attribute__((always_inline)) {
+          const float nm = m == -__builtin_inff() ? 0.f : -m;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) O[db] *= alpha;
+          for (int v = 0; v < 16; ++v) pr[v] = fast_exp2(fmaf(S[v], a.scale_log2, nm));
+        };
+        auto row_sum = [&]() __attribute__((always_inline)) {
+          const float s0 = (pr[0] + pr[4]) + (pr[8] + pr[12]), s1 = (pr[1] + pr[5]) + (pr[9] + pr[13]);
+          const float s2 = (pr[2] + pr[6]) + (pr[10] + pr[14]), s3 = (pr[3] + pr[7]) + (pr[11] + pr[15]);
+          return (s0 + s1) + (s2 + s3);
+        };
+        probs();
+        float ls = row_sum();
+        if (__any(!(ls <= 256.0f) || m == -__builtin_inff())) {
+          float mx0 = fmaxf(fmaxf(S[0], S[1]), S[2]), mx1 = fmaxf(fmaxf(S[3], S[4]), S[5]);
+          float mx2 = fmaxf(fmaxf(S[6], S[7]), S[8]), mx3 = fmaxf(fmaxf(S[9], S[10]), S[11]);
+          float mx4 = fmaxf(fmaxf(S[12], S[13]), S[14]);
+          float mx = fmaxf(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3)), fmaxf(mx4, S[15]));
+          mx = half_max(mx) * a.scale_log2;
+          if (__any(mx > m + 8.0f)) {
+            const float mn = fmaxf(m, mx);
+            const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mn);
+            m = mn;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) O[db] *= alpha;
+            probs();
+            ls = row_sum();
+          }
         }
-        // Probabilities: the row sum adds them in fp32 (four partial sums), the
-        // P.V product takes them rounded to bf16.
-        const float nm = m == -__builtin_inff() ? 0.f : -m;
         bf16x8 P[2];
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(fmaf(S[v], a.scale_log2, nm));
-          ls[v & 3] += p;
-          P[v >> 3][v & 7] = (__bf16)p;
-        }
-        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        for (int v = 0; v < 16; ++v) P[v >> 3][v & 7] = (__bf16)pr[v];
+        l += ls;
         // K fragments of the next sub-tile of this tile, read while P.V runs.
         if (st == 0 && nvalid > 32) load_k(Ks + 32 * D);
         // O^T += V^T . P^T over the two 16-token k-chunks of this sub-tile.
