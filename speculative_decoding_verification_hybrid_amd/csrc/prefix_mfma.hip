@@ -21,8 +21,8 @@
 // refilled. The copies are issued from inline assembly, so the compiler's wait
 // insertion never sees them (it would otherwise drain the whole copy queue
 // before LDS reads it cannot prove disjoint from a copy in flight); every wait
-// on them is explicit, and the only compiler-issued vector loads (the Q
-// fragments) complete before the first copy of a piece.
+// on them is explicit (the Q fragments are loaded the same way, just before
+// the first copies of a piece).
 //
 // One copy instruction moves 1 KB: 4 (D = 128) or 8 (D = 64) whole rows of K
 // or V, read coalesced from HBM, with the lanes' 16-byte chunks permuted on
@@ -248,18 +248,19 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
     }
 
     // Q^T fragments (B operand of S^T = K.Q^T): row `row`, dims 16c + 8hh .. +7.
+    // Loaded from inline assembly, like the tile copies, so that one explicit
+    // wait covers both: they are queued before the first tiles' copies and are
+    // complete once tile 0 is. Rows past the limit load row 0 and are zeroed.
     bf16x8 qf[KC];
     {
       const unsigned short* qr = qp + (size_t)(row_ok ? row : 0) * D + 8 * hh;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        u32x4 r = *(const u32x4*)(qr + 16 * c);
-        if (!row_ok) r = u32x4{0u, 0u, 0u, 0u};
+        u32x4 r;
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(qr + 16 * c) : "memory");
         qf[c] = __builtin_bit_cast(bf16x8, r);
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());  // Q is in registers before any copy is queued
-
     // Queue the copies of tile t of the piece into stage t % NSTAGE: this
     // wave's NBH blocks of K and NBH blocks of V. Rows past the tile's valid
     // tokens repeat its last valid row, so every value read is finite and in
@@ -312,7 +313,17 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
     // Every stage starts filled: tile t goes to stage t % NSTAGE, and the stage
     // of tile t is refilled (with tile t + NSTAGE) once tile t is consumed.
     for (int t = 0; t < min(ntiles, NSTAGE); ++t) copy_tile(t);
-    wait_tiles(min(ntiles, NSTAGE) - 1);
+    wait_tiles(min(ntiles, NSTAGE) - 1);  // tile 0 and the older Q loads have landed
+    // Tie the Q registers to the wait: nothing below may read them earlier.
+    // (The compiler still could copy them between the load and here; the CPU
+    // test tests/test_q_load_isa.py checks the generated code for that.)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 r = __builtin_bit_cast(u32x4, qf[c]);
+      asm volatile("" : "+v"(r));
+      if (!row_ok) r = u32x4{0u, 0u, 0u, 0u};
+      qf[c] = __builtin_bit_cast(bf16x8, r);
+    }
     tile_barrier();
     if (computes) load_k(lds);
 
