@@ -102,6 +102,7 @@ typedef struct {
   float softmax_scale;    /* <= 0 selects 1/sqrt(D) */
   int32_t num_workgroups; /* prefix-kernel workgroups; 0 = sized from the device */
   int32_t force_path;     /* enum hta_path; AUTO picks MFMA for bf16 with G*T >= 16 */
+  int32_t qblocks_per_wave; /* MFMA path: 32-row query blocks per wave, 1 or 2; 0 = planned */
 } hta_config_t;
 
 typedef struct {

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhta.so")
-SOURCES = ["hta_api.hip", "prefix_mfma.hip", "prefix_valu.hip", "tree.hip", "merge.hip"]
+SOURCES = ["hta_api.hip", "prefix_mfma.hip", "prefix_mfma2.hip", "prefix_valu.hip", "tree.hip", "merge.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 instructions (the host
@@ -29,6 +29,15 @@ CFLAGS = [
 ]
 
 
+# Per-source additions: the two-block split-KV kernel wants MFMA results in
+# VGPRs (its scores go straight into VALU softmax code).
+FILE_FLAGS = {"prefix_mfma2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def flags_for(src: str) -> list:
+    return CFLAGS + FILE_FLAGS.get(src, [])
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -38,7 +47,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags_for(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")

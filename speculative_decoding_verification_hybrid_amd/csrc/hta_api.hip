@@ -46,6 +46,7 @@ int validate(const hta_config_t* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return HTA_ERR_UNSUPPORTED;
   if (c->tree_nodes > 64) return HTA_ERR_UNSUPPORTED;
   if (c->force_path == HTA_PATH_MFMA && c->dtype != HTA_BF16) return HTA_ERR_UNSUPPORTED;
+  if (c->qblocks_per_wave < 0 || c->qblocks_per_wave > 2) return HTA_ERR_INVALID_ARG;
   // Index arithmetic limits: rows and per-sequence KV spans stay within int32.
   const int64_t rows = (int64_t)c->batch * c->n_q_heads * c->tree_nodes;
   if (rows * c->head_dim > INT32_MAX) return HTA_ERR_UNSUPPORTED;
@@ -54,21 +55,26 @@ int validate(const hta_config_t* c) {
   return HTA_OK;
 }
 
-// Split-KV kernel shape: MFMA path blocks of 32 query rows, one per wave,
-// at most 8 waves per workgroup (more rows use more row groups); VALU path
-// 16 rows per workgroup.
-void plan_rows(const hta::Dims& d, int path, hta::PrefixLaunch* pl) {
+// Split-KV kernel shape. MFMA path: query rows in blocks of 32; a wave owns
+// qb blocks (qb = 1: at most 8 waves per workgroup; qb = 2: one wave per SIMD,
+// at most 4); more rows than one workgroup holds go to further row groups
+// (grid.y). The plan takes qb = 1: with a single wave per SIMD the two-block
+// kernel's instruction issue (its LDS reads in particular) is not hidden, and
+// it measures slower at the shapes benchmarked; qb = 2 is taken on request.
+// VALU path: 16 rows per workgroup.
+void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) {
   pl->path = path;
   if (path == HTA_PATH_MFMA) {
-    // one wave per 32-row q-block, up to 8 per workgroup; more rows go to
-    // further row groups (grid.y)
     const int nqb = (d.M + 31) / 32;
-    const int rg = (nqb + 7) / 8;
-    const int per = (nqb + rg - 1) / rg;
+    const int qb = qb_req > 0 ? qb_req : 1;
+    const int nwb = (nqb + qb - 1) / qb;   // wave-sized row blocks
+    const int maxw = qb == 2 ? 4 : 8;
+    const int rg = (nwb + maxw - 1) / maxw;
+    const int per = (nwb + rg - 1) / rg;
     pl->row_groups = rg;
-    pl->rows_per_group = per * 32;
+    pl->rows_per_group = per * 32 * qb;
     pl->waves = per;
-    pl->qb = 1;
+    pl->qb = qb;
   } else {
     pl->row_groups = (d.M + 15) / 16;
     pl->rows_per_group = 16;
@@ -137,7 +143,7 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
 
   int path = cfg->force_path;
   if (path == HTA_PATH_AUTO) path = (d.bf16 && d.M >= 16) ? HTA_PATH_MFMA : HTA_PATH_VALU;
-  plan_rows(d, path, &h->pl);
+  plan_rows(d, path, cfg->qblocks_per_wave, &h->pl);
   if (path == HTA_PATH_MFMA && !hta::prefix_mfma_supported(d.D, h->pl.waves, h->pl.qb)) {
     delete h;
     return HTA_ERR_UNSUPPORTED;

@@ -55,95 +55,12 @@
 // bounds every term), which after the first sub-tile is rare.
 #include <type_traits>
 
-#include "common.h"
 #include "hta_internal.h"
+#include "prefix_mfma_common.h"
 
 namespace hta {
+namespace mfma {
 namespace {
-
-constexpr int NK = kTileTokens;
-constexpr int NSTAGE = 4;
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-struct PrefixArgs {
-  const unsigned short* q;
-  const unsigned short* k;
-  const unsigned short* v;
-  const unsigned short* kt;  // tree keys (fused tree part) or null
-  const unsigned short* vt;
-  const int* parent;
-  const int* prefix_len;
-  unsigned short* slot_o;  // bf16 partials
-  float* slot_lse2;
-  int* err_b;
-  int* status;
-  int B, Hq, Hkv, G, T, Lcap, M;
-  int nwg, rows_per_group, tree_tiles;
-  float scale_log2;
-};
-
-// XOR swizzle of the 16-byte chunks of K row r. D = 128: a row spans all 64
-// banks and the swizzle is a bijection of r's low 4 bits, so the 16 rows of a
-// K fragment read hit 16 different chunks. D = 64: two rows share the banks,
-// and the same holds per half.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-// MFMA row -> token within a 32-token sub-tile: swap bits 2 and 3.
-__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
-
-__device__ __forceinline__ i16x4 lds_read_tr(const unsigned short* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-}
-
-// Cross-half (lane l <-> l ^ 32) max and sum in VALU: the two results of the
-// lane swap are this lane's value and its partner's, in some order.
-__device__ __forceinline__ float half_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(fmaxf(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding: vmcnt
-// in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maximum).
-template <int N>
-constexpr int vmcnt_only() {
-  return (N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8);
-}
-constexpr int kLgkmZero = 15 | (7 << 4) | (3 << 14);  // lgkmcnt(0) only
-
-// Workgroup barrier that orders LDS accesses only in the compiler: the
-// hardware waits for the tile copies are the explicit ones before it (a memory
-// fence here would drain every copy in flight).
-__device__ __forceinline__ void tile_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One 16-byte-per-lane copy from global memory into LDS: lane i reads the 16
-// bytes at base + off (base wave-uniform, in SGPRs; off a 32-bit per-lane byte
-// offset) and they land at LDS byte address lds_base + 16 i. lds_base must be
-// wave-uniform (it goes through M0, which needs one wait state before the
-// copy). The "memory" clobber keeps the compiler from moving LDS accesses
-// across the copy.
-__device__ __forceinline__ void copy16_to_lds(const void* base, unsigned off, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(lds_base)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ unsigned lds_addr(const unsigned short* p) {
-  return (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned short*)p;
-}
 
 // Threads per workgroup: the WQ compute waves plus copy-only waves up to 4
 // (WQ <= 4) or 8.
@@ -474,8 +391,6 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
   }
 }
 
-typedef void (*KernelFn)(PrefixArgs);
-
 template <int D>
 KernelFn pick_d(int wq) {
   switch (wq) {
@@ -492,13 +407,20 @@ KernelFn pick_d(int wq) {
 }
 
 KernelFn pick(int D, int waves, int qb) {
+  if (qb == 2) return prefix_mfma2_pick(D, waves);
   if (qb != 1) return nullptr;
   return D == 128 ? pick_d<128>(waves) : D == 64 ? pick_d<64>(waves) : nullptr;
 }
 
-int threads_of(int waves) { return waves <= 4 ? 256 : 512; }
+int threads_of(int waves, int qb) { return qb == 2 || waves <= 4 ? 256 : 512; }
 
 }  // namespace
+}  // namespace mfma
+
+using mfma::KernelFn;
+using mfma::PrefixArgs;
+using mfma::pick;
+using mfma::threads_of;
 
 bool prefix_mfma_supported(int D, int waves, int qb) { return pick(D, waves, qb) != nullptr; }
 
@@ -506,7 +428,7 @@ int prefix_mfma_occupancy(int D, int waves, int qb) {
   KernelFn k = pick(D, waves, qb);
   if (!k) return 0;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), threads_of(waves), 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), threads_of(waves, qb), 0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;
@@ -539,7 +461,7 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
   a.rows_per_group = pl.rows_per_group;
   a.tree_tiles = in.k_tree ? 1 : 0;
   a.scale_log2 = d.scale_log2;
-  hipLaunchKernelGGL(k, dim3(pl.nwg, pl.row_groups), dim3(threads_of(pl.waves)), 0, s, a);
+  hipLaunchKernelGGL(k, dim3(pl.nwg, pl.row_groups), dim3(threads_of(pl.waves, pl.qb)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ class HtaConfig(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("num_workgroups", ctypes.c_int32),
         ("force_path", ctypes.c_int32),
+        ("qblocks_per_wave", ctypes.c_int32),
     ]
 
 
@@ -135,10 +136,11 @@ def hta_status_string(code: int) -> str:
 
 
 def make_config(*, batch, n_q_heads, n_kv_heads, head_dim, tree_nodes, kv_capacity, dtype="bf16",
-                softmax_scale=0.0, num_workgroups=0, force_path=HTA_PATH_AUTO) -> HtaConfig:
+                softmax_scale=0.0, num_workgroups=0, force_path=HTA_PATH_AUTO,
+                qblocks_per_wave=0) -> HtaConfig:
     dt = {"bf16": HTA_BF16, "f32": HTA_F32, HTA_BF16: HTA_BF16, HTA_F32: HTA_F32}[dtype]
     return HtaConfig(batch, n_q_heads, n_kv_heads, head_dim, tree_nodes, kv_capacity, dt,
-                     float(softmax_scale), num_workgroups, force_path)
+                     float(softmax_scale), num_workgroups, force_path, qblocks_per_wave)
 
 
 def hta_validate_config(cfg: HtaConfig) -> int:

@@ -285,3 +285,46 @@ def test_bad_prefix_len_gives_nan_rows_and_status(bad_len):
     assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
     ref_out, ref_lse = oracle.verify_attn(w, batches=[0])
     assert_close(w, out, lse, ref_out, ref_lse)
+
+
+# ----------------------------------------------------------------------------
+# both MFMA kernels (one or two 32-row query blocks per wave) on every shape
+# ----------------------------------------------------------------------------
+
+KERNEL_SHAPES = {
+    "m256": dict(B=2, Hq=32, Hkv=8, D=128, Lcap=1500, T=64, prefix_len=[1500, 777]),
+    "m64_copy_waves": dict(B=2, Hq=4, Hkv=1, D=128, Lcap=700, T=16, prefix_len=[700, 65]),
+    "m160_half_block": dict(B=2, Hq=10, Hkv=2, D=128, Lcap=1100, T=32, prefix_len=[1100, 613]),
+    "m512_two_groups": dict(B=1, Hq=16, Hkv=2, D=128, Lcap=640, T=64, prefix_len=[640]),
+    "d64_m64": dict(B=2, Hq=16, Hkv=4, D=64, Lcap=900, T=16, prefix_len=[900, 450]),
+    "d64_m256": dict(B=1, Hq=16, Hkv=4, D=64, Lcap=600, T=64, prefix_len=[555]),
+    "ragged_t33": dict(B=6, Hq=8, Hkv=2, D=128, Lcap=1000, T=33, prefix_len=[1, 63, 64, 65, 1000, 0]),
+    "poison_tail": dict(B=3, Hq=8, Hkv=2, D=128, Lcap=500, T=16, prefix_len=[77, 500, 1], poison_tail=True),
+    "drift_keys": dict(B=1, Hq=32, Hkv=8, D=128, Lcap=3000, T=32, prefix_len=[3000], drift=True,
+                       tree=("bounded", 8, None)),
+}
+
+
+@pytest.mark.parametrize("qb", [1, 2])
+@pytest.mark.parametrize("name", sorted(KERNEL_SHAPES))
+def test_mfma_kernel_parity(name, qb):
+    w = make_custom(seed=zlib.crc32(name.encode()) % 1000, dtype="bf16", **KERNEL_SHAPES[name])
+    say(f"mfma kernel qb={qb} {name}: hta_verify_attn")
+    out, lse, status = run_verify(w, force_path=hta.HTA_PATH_MFMA, qblocks_per_wave=qb)
+    assert status == 0
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ref_out, ref_lse = oracle.verify_attn(w)
+    eo, el = assert_close(w, out, lse, ref_out, ref_lse)
+    say(f"mfma kernel qb={qb} {name}: out err {eo:.2e}, lse rel err {el:.2e}")
+
+
+@pytest.mark.parametrize("qb", [1, 2])
+@pytest.mark.parametrize("nwg", [1, 7, 1000])
+def test_mfma_kernel_pieces(qb, nwg):
+    """Workgroups spanning several segments, and many one-tile pieces."""
+    w = make_custom(B=4, Hq=32, Hkv=4, D=128, Lcap=1500, T=24, prefix_len=[1500, 64, 999, 1], seed=40 + nwg)
+    say(f"mfma kernel qb={qb} num_workgroups={nwg}")
+    out, lse, status = run_verify(w, num_workgroups=nwg, force_path=hta.HTA_PATH_MFMA, qblocks_per_wave=qb)
+    assert status == 0
+    ref_out, ref_lse = oracle.verify_attn(w)
+    assert_close(w, out, lse, ref_out, ref_lse)

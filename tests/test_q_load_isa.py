@@ -23,7 +23,7 @@ import pytest
 from speculative_decoding_verification_hybrid_amd import _build
 
 VMEM = re.compile(r"^\s*(global_|buffer_|flat_|scratch_)(load|store|atomic)")
-KERNEL = re.compile(r"^(_ZN3hta12_GLOBAL__N_118prefix_mfma_kernelILi(\d+)ELi(\d+)E\S*):", re.M)
+KERNEL = re.compile(r"^(_ZN3hta4mfma12_GLOBAL__N_11[89]prefix_mfma2?_kernelILi(\d+)ELi(\d+)E\S*):", re.M)
 
 
 def _regs(line):
@@ -77,15 +77,16 @@ def check_kernel(body):
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-def test_q_fragment_loads_untouched_until_waited(tmp_path):
-    out = tmp_path / "prefix_mfma.s"
-    cmd = [_build.hipcc()] + _build.CFLAGS + ["--cuda-device-only", "-S",
-                                              os.path.join(_build.CSRC, "prefix_mfma.hip"), "-o", str(out)]
+@pytest.mark.parametrize("src,instances", [("prefix_mfma.hip", 16), ("prefix_mfma2.hip", 8)])
+def test_q_fragment_loads_untouched_until_waited(tmp_path, src, instances):
+    out = tmp_path / (src + ".s")
+    cmd = [_build.hipcc()] + _build.flags_for(src) + ["--cuda-device-only", "-S", os.path.join(_build.CSRC, src),
+                                                      "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     s = out.read_text()
     kernels = list(KERNEL.finditer(s))
-    assert len(kernels) >= 2
+    assert len(kernels) == instances  # every (D, waves) instance
     for m in kernels:
         end = s.index("s_endpgm", m.end())
         body = [l for l in s[m.end():end].split("\n") if l.strip() and not l.strip().startswith(";")
