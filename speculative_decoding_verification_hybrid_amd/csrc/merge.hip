@@ -62,7 +62,10 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   const int pg = lane / LPR;
   const int dl = lane % LPR;
   const int64_t rows_total = (int64_t)a.B * a.Hq * a.T;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // Rows are ordered (b, head, node), so a (sequence, KV head) segment's rows
+  // are contiguous; the same XCD mapping as the split-KV kernel puts them on
+  // the XCD whose L2 holds that segment's partials.
+  const int64_t row = (int64_t)xcd_remap((int)blockIdx.x, (int)gridDim.x) * 4 + (threadIdx.x >> 6);
   if (row >= rows_total) return;
   const int b = (int)(row / ((int64_t)a.Hq * a.T));
   const int rem = (int)(row % ((int64_t)a.Hq * a.T));
@@ -213,9 +216,11 @@ MergeArgs base_args(const Dims& d) {
   return a;
 }
 
+// Four rows per workgroup, rounded up to a multiple of 8 workgroups (one per
+// XCD) so that xcd_remap applies.
 unsigned grid_for(const Dims& d) {
   const int64_t rows = (int64_t)d.B * d.Hq * d.T;
-  return (unsigned)((rows + 3) / 4);
+  return (unsigned)(((rows + 3) / 4 + 7) / 8 * 8);
 }
 
 }  // namespace
