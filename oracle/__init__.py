@@ -15,3 +15,4 @@ from .hta_oracle import (  # noqa: F401
     tree_visible_nodes,
     verify_attn,
 )
+from .accept_oracle import accept, accept_path, commit, target_tokens  # noqa: F401,E402
