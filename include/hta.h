@@ -86,7 +86,12 @@ enum hta_status_code {
 enum hta_dtype { HTA_F32 = 0, HTA_BF16 = 1 };
 
 /* Bits of the device status word (see hta_get_status). */
-enum hta_device_status { HTA_STATUS_BAD_TREE = 1, HTA_STATUS_BAD_PREFIX = 2 };
+enum hta_device_status {
+  HTA_STATUS_BAD_TREE = 1,
+  HTA_STATUS_BAD_PREFIX = 2,
+  HTA_STATUS_COMMIT_OVERFLOW = 4, /* hta_commit: prefix_len + accept_len would pass kv_capacity */
+  HTA_STATUS_BAD_PATH = 8         /* hta_commit: an accept_path entry outside [0, T) */
+};
 
 /* Prefix-kernel implementation (see hta_plan_t.path). */
 enum hta_path { HTA_PATH_AUTO = 0, HTA_PATH_MFMA = 1, HTA_PATH_VALU = 2 };
@@ -187,6 +192,44 @@ HTA_API int hta_merge_prefix(hta_handle_t h, const int32_t* prefix_len, float* o
  * LongSpec, "Fast Tree Attention" (aggregation with the log-sum-exp trick). */
 HTA_API int hta_lse_merge(hta_handle_t h, int32_t n_parts, const float* o_parts, const float* lse_parts,
                   float* out, float* lse, void* stream);
+
+/* Accepts the verified draft tree of every sequence (LogitSpec, "draft tree
+ * construction and verification": a tree rooted at x_{i+1} whose branches the
+ * target checks at once; LongSpec: lossless decoding keeps only what the target
+ * itself would produce). Greedy reading:
+ *   target_tokens[b][j] = argmax_v logits[b][j][v], the lowest v among equal
+ *     maxima, on the exact stored values (finite logits);
+ *   from the root (node 0, always accepted) the walk moves to the child whose
+ *     tree token equals the target token at its parent, the lowest-numbered
+ *     such child, until no child matches;
+ *   accept_len[b] = accepted nodes (root included), accept_path[b][k] = the
+ *     k-th of them root first (-1 from accept_len[b] on), bonus_token[b] =
+ *     target_tokens[b][last accepted node].
+ * logits [B,T,vocab] of logits_dtype (HTA_F32 or HTA_BF16, any alignment;
+ * 16-byte aligned rows take the vector path); parent, tree_tokens,
+ * target_tokens, accept_path [B,T] int32; accept_len, bonus_token [B] int32;
+ * all device pointers owned by the caller. A sequence whose parent array
+ * breaks -1 <= parent[i] < i gets accept_len 0, an all -1 path, bonus -1
+ * and HTA_STATUS_BAD_TREE. Uses the handle's workspace (one call in flight
+ * per handle). */
+HTA_API int hta_accept(hta_handle_t h, const void* logits, int32_t vocab, int32_t logits_dtype,
+                       const int32_t* parent, const int32_t* tree_tokens, int32_t* target_tokens,
+                       int32_t* accept_len, int32_t* accept_path, int32_t* bonus_token, void* stream);
+
+/* Commits the accepted nodes of the last verification: for every sequence b
+ * with 0 < accept_len[b] and prefix_len[b] + accept_len[b] <= kv_capacity,
+ * copies k_tree[b][g][accept_path[b][k]] and v_tree[...] to
+ * k_cache[b][g][prefix_len[b] + k] and v_cache[...] for every KV head g and
+ * k < accept_len[b], then advances prefix_len[b] (device, in place) by
+ * accept_len[b]. Other sequences are left unchanged; one that would overflow
+ * raises HTA_STATUS_COMMIT_OVERFLOW, a path entry outside [0, T) raises
+ * HTA_STATUS_BAD_PATH (that row is skipped). k_tree, v_tree [B,Hkv,T,D] and
+ * k_cache, v_cache [B,Hkv,Lcap,D] have the handle's dtype and must be 16-byte
+ * aligned. The accepted tokens' keys and values join the cached part that
+ * the next verification reads unmasked (LongSpec, "Fast Tree Attention"). */
+HTA_API int hta_commit(hta_handle_t h, const void* k_tree, const void* v_tree, const int32_t* accept_len,
+                       const int32_t* accept_path, void* k_cache, void* v_cache, int32_t* prefix_len,
+                       void* stream);
 
 /* Synchronises `stream`, returns in *device_status the OR of the status
  * bits raised since the last call (HTA_STATUS_*), and clears them. */

@@ -30,6 +30,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kStatusBadTree = 1;
 constexpr int kStatusBadPrefix = 2;
+constexpr int kStatusCommitOverflow = 4;
+constexpr int kStatusBadPath = 8;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -18,6 +18,7 @@ struct hta_handle_s {
   hta::Slots slots;
   int* err_b;        // [B] bad-tree flags of the last call
   int* status;       // sticky HTA_STATUS_* bits
+  unsigned long long* argmax_part;  // [B*T*kArgmaxMaxSplit] partial argmax keys (hta_accept)
 };
 
 namespace {
@@ -176,6 +177,8 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   off = align256(off + (size_t)max_slots * d.M * d.D * (slot_bf16 ? 2 : 4));
   const size_t off_sl = off;
   off = align256(off + (size_t)max_slots * d.M * sizeof(float));
+  const size_t off_ap = off;
+  off = align256(off + (size_t)d.B * d.T * hta::kArgmaxMaxSplit * sizeof(unsigned long long));
   const size_t off_eb = off;
   off = align256(off + (size_t)d.B * sizeof(int));
   const size_t off_st = off;
@@ -191,6 +194,7 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   h->slots.lse2 = reinterpret_cast<float*>(base + off_sl);
   h->err_b = reinterpret_cast<int*>(base + off_eb);
   h->status = reinterpret_cast<int*>(base + off_st);
+  h->argmax_part = reinterpret_cast<unsigned long long*>(base + off_ap);
   if (hipMemset(base + off_eb, 0, off - off_eb) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws);
@@ -291,6 +295,27 @@ int hta_lse_merge(hta_handle_t h, int32_t n_parts, const float* o_parts, const f
   if (!all_aligned(o_parts, out)) return HTA_ERR_INVALID_ARG;
   return check_hip(hta::launch_merge_parts(h->dims, n_parts, o_parts, lse_parts, out, lse,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int hta_accept(hta_handle_t h, const void* logits, int32_t vocab, int32_t logits_dtype, const int32_t* parent,
+               const int32_t* tree_tokens, int32_t* target_tokens, int32_t* accept_len, int32_t* accept_path,
+               int32_t* bonus_token, void* stream) {
+  if (!h || !logits || !parent || !tree_tokens || !target_tokens || !accept_len || !accept_path || !bonus_token)
+    return HTA_ERR_INVALID_ARG;
+  if (vocab < 1 || (logits_dtype != HTA_F32 && logits_dtype != HTA_BF16)) return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_accept(h->dims, logits, vocab, logits_dtype == HTA_BF16, parent, tree_tokens,
+                                      h->argmax_part, target_tokens, accept_len, accept_path, bonus_token,
+                                      h->status, static_cast<hipStream_t>(stream)));
+}
+
+int hta_commit(hta_handle_t h, const void* k_tree, const void* v_tree, const int32_t* accept_len,
+               const int32_t* accept_path, void* k_cache, void* v_cache, int32_t* prefix_len, void* stream) {
+  if (!h || !k_tree || !v_tree || !accept_len || !accept_path || !k_cache || !v_cache || !prefix_len)
+    return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(k_tree, v_tree, static_cast<const void*>(k_cache), static_cast<const void*>(v_cache)))
+    return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_commit(h->dims, k_tree, v_tree, accept_len, accept_path, k_cache, v_cache,
+                                      prefix_len, h->status, static_cast<hipStream_t>(stream)));
 }
 
 int hta_get_status(hta_handle_t h, void* stream, int32_t* device_status) {

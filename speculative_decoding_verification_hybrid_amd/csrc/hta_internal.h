@@ -78,4 +78,15 @@ hipError_t launch_merge_parts(const Dims& d, int n_parts, const float* o_parts,
 
 hipError_t launch_clear_status(int* status, hipStream_t s);
 
+// Accept / commit of a verified draft tree (accept.hip). The argmax over the
+// vocabulary splits each logit row over at most kArgmaxMaxSplit workgroups;
+// part holds B*T*kArgmaxMaxSplit keys.
+constexpr int kArgmaxMaxSplit = 64;
+hipError_t launch_accept(const Dims& d, const void* logits, int V, bool logits_bf16, const int* parent,
+                         const int* tree_tokens, unsigned long long* part, int* target_out, int* accept_len,
+                         int* accept_path, int* bonus, int* status, hipStream_t s);
+hipError_t launch_commit(const Dims& d, const void* k_tree, const void* v_tree, const int* accept_len,
+                         const int* accept_path, void* k_cache, void* v_cache, int* prefix_len, int* status,
+                         hipStream_t s);
+
 }  // namespace hta

@@ -34,6 +34,8 @@ HTA_BF16 = 1
 
 HTA_STATUS_BAD_TREE = 1
 HTA_STATUS_BAD_PREFIX = 2
+HTA_STATUS_COMMIT_OVERFLOW = 4
+HTA_STATUS_BAD_PATH = 8
 
 HTA_PATH_AUTO = 0
 HTA_PATH_MFMA = 1
@@ -92,6 +94,8 @@ _SIGNATURES = {
     "hta_prefix_partials": (ctypes.c_int, [_vp] * 5 + [_vp]),
     "hta_merge_prefix": (ctypes.c_int, [_vp] * 4 + [_vp]),
     "hta_lse_merge": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "hta_accept": (ctypes.c_int, [_vp, _vp, _i32, _i32] + [_vp] * 6 + [_vp]),
+    "hta_commit": (ctypes.c_int, [_vp] * 8 + [_vp]),
     "hta_get_status": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(_i32)]),
     "hta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -315,6 +319,48 @@ def hta_lse_merge(h: Handle, o_parts, lse_parts, out, lse, stream=None) -> None:
     ]
     _check(load_library().hta_lse_merge(_vp(h.ptr), n, *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
            "hta_lse_merge")
+
+
+def hta_accept(h: Handle, logits, parent, tree_tokens, target_tokens, accept_len, accept_path, bonus_token,
+               stream=None) -> None:
+    """logits [B, T, V] float32 or bfloat16; the int32 tensors as in include/hta.h."""
+    import torch
+    B, _, _, _, T, _ = h.dims
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 3:
+        raise ValueError("logits must be a [B, T, V] tensor")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"logits has dtype {logits.dtype}, expected float32 or bfloat16")
+    V = int(logits.shape[2])
+    ldt = HTA_BF16 if logits.dtype == torch.bfloat16 else HTA_F32
+    args = [
+        _tensor(parent, "parent", torch.int32, (B, T)),
+        _tensor(tree_tokens, "tree_tokens", torch.int32, (B, T)),
+        _tensor(target_tokens, "target_tokens", torch.int32, (B, T)),
+        _tensor(accept_len, "accept_len", torch.int32, (B,)),
+        _tensor(accept_path, "accept_path", torch.int32, (B, T)),
+        _tensor(bonus_token, "bonus_token", torch.int32, (B,)),
+    ]
+    lp = _tensor(logits, "logits", logits.dtype, (B, T, V))
+    _check(load_library().hta_accept(_vp(h.ptr), _vp(lp), V, ldt, *[_vp(a) for a in args],
+                                     _vp(_stream_ptr(stream))), "hta_accept")
+
+
+def hta_commit(h: Handle, k_tree, v_tree, accept_len, accept_path, k_cache, v_cache, prefix_len,
+               stream=None) -> None:
+    import torch
+    B, _, Hkv, D, T, Lcap = h.dims
+    dt = _io_dtype(h)
+    args = [
+        _tensor(k_tree, "k_tree", dt, (B, Hkv, T, D)),
+        _tensor(v_tree, "v_tree", dt, (B, Hkv, T, D)),
+        _tensor(accept_len, "accept_len", torch.int32, (B,)),
+        _tensor(accept_path, "accept_path", torch.int32, (B, T)),
+        _tensor(k_cache, "k_cache", dt, (B, Hkv, Lcap, D)),
+        _tensor(v_cache, "v_cache", dt, (B, Hkv, Lcap, D)),
+        _tensor(prefix_len, "prefix_len", torch.int32, (B,)),
+    ]
+    _check(load_library().hta_commit(_vp(h.ptr), *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
+           "hta_commit")
 
 
 def hta_get_status(h: Handle, stream=None) -> int:

@@ -101,6 +101,8 @@ def test_null_arguments_fail_before_any_hip_call(lib):
     assert lib.hta_prefix_partials(None, *([None] * 5)) == hta.HTA_ERR_INVALID_ARG
     assert lib.hta_merge_prefix(None, *([None] * 4)) == hta.HTA_ERR_INVALID_ARG
     assert lib.hta_get_status(None, None, None) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_accept(None, None, 100, hta.HTA_BF16, *([None] * 7)) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_commit(None, *([None] * 8)) == hta.HTA_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

@@ -19,3 +19,4 @@ from .gen import (  # noqa: F401
     tree_star,
     tree_uniform,
 )
+from .accept_gen import AcceptCase, make_accept_case  # noqa: F401,E402
