@@ -17,7 +17,10 @@ Prints one JSON line. ``value`` is the layer's achieved HBM bandwidth on its
 algorithmic bytes (valid KV read once + q, tree K/V, out, lse, tree shape);
 beside it: the per-layer latency, verified tokens/s, the split-KV kernel's
 roofline (its K launches captured and timed the same way, alone) and the fp64
-CPU oracle's throughput on a bounded sample of the same workload.
+CPU oracle's throughput on a bounded sample of the same workload. A second
+leg ("accept_commit") times hta_accept + hta_commit on the same draft tree
+with bf16 target logits over a 128256-token vocabulary, the same way, with
+the oracle's accept + commit on the same inputs beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --copy-calibration   (adds 8 launches of a plain elementwise
@@ -41,8 +44,11 @@ METRIC = ("verify-attn layer µs + achieved HBM GB/s (% peak), 8B GQA shape, 32k
           "64-node tree")
 PEAK_HBM_GBS = 8000.0
 WORKLOAD_KEY = 3
+CSRC = os.path.join(ROOT, "speculative_decoding_verification_hybrid_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_mfma_llama8b_32k_traffic.txt")
-PREFIX_SRC = os.path.join(ROOT, "speculative_decoding_verification_hybrid_amd", "csrc", "prefix_mfma.hip")
+PREFIX_SRC = os.path.join(CSRC, "prefix_mfma.hip")
+ACCEPT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "argmax_accept_llama8b_vocab128k_traffic.txt")
+ACCEPT_SRC = os.path.join(CSRC, "accept.hip")
 
 
 def parse():
@@ -55,6 +61,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the CPU oracle baseline")
+    ap.add_argument("--no-accept", action="store_true", help="skip the accept + commit leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 8 copy-like 256 MiB elementwise kernels before timing")
     return ap.parse_args()
@@ -70,21 +77,21 @@ def algorithmic_bytes(w):
     return kv, kv + tree_kv + q_out + lse + meta
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the split-KV kernel from a committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_from_profile(path=TRAFFIC_FILE, src=PREFIX_SRC, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    for ln in open(TRAFFIC_FILE):
+    for ln in open(path):
         if "=" in ln and not ln.startswith("#"):
             k, v = ln.split("=", 1)
             fields[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(PREFIX_SRC, "rb").read()).hexdigest()[:16]
+    src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if fields.get("kernel_source_sha256_16") != src_hash:
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
 
@@ -92,11 +99,7 @@ def traffic_from_profile():
 def cpu_baseline(w, min_seconds):
     """The fp64 oracle on the same workload, repeated until min_seconds of wall time."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = _cores()
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -111,6 +114,137 @@ def cpu_baseline(w, min_seconds):
             "sample": f"the whole workload (all {w.Hq} query heads, {w.T} tree nodes, "
                       f"{int(w.prefix_len[0])}-token prefix) {reps} times, {dt:.2f} s wall, "
                       f"{dt / reps * 1e3:.1f} ms per layer"}
+
+
+VOCAB = 128256  # Llama-3.1-8B vocabulary
+
+
+def accept_commit_row(w, steps, warmup, replica_bytes, cpu_seconds):
+    """hta_accept + hta_commit on the same draft tree with bf16 target logits over a
+    Llama-3.1-8B vocabulary: [B, T, V] logits rotated over >= replica_bytes of copies
+    (cold in the Infinity Cache), a fresh prefix_len per step so every step commits
+    at the same place, and a cache with room behind the prefix for two replays of the
+    graph of steps (each step's prefix_len advances once per replay)."""
+    import torch
+    from speculative_decoding_verification_hybrid_amd import hta
+    from workloads import make_accept_case
+
+    case = make_accept_case(B=w.B, T=w.T, V=VOCAB, dtype="bf16", seed=1234, parents=w.parent,
+                            depth=[5] * w.B)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    lg0 = torch.from_numpy(case.logits.view(np.int16)).view(torch.bfloat16).cuda()
+    logit_bytes = lg0.numel() * 2
+    R = max(1, int(np.ceil(replica_bytes / logit_bytes)))
+    lgs = [lg0] + [lg0.clone() for _ in range(R - 1)]
+    parent, tokens = i32(case.parent), i32(case.tree_tokens)
+    Lcap = int(w.prefix_len.max()) + 2 * w.T  # the graph of steps replays twice (upload, timed)
+    kc = torch.zeros(w.B, w.Hkv, Lcap, w.D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    kt, vt = bits(w.k_tree), bits(w.v_tree)
+    target = torch.empty(w.B, w.T, dtype=torch.int32, device="cuda")
+    n = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    path = torch.empty(w.B, w.T, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    plen0 = i32(w.prefix_len)
+    plens = [plen0.clone() for _ in range(warmup + steps)]
+    cfg = hta.make_config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, tree_nodes=w.T,
+                          kv_capacity=Lcap, dtype="bf16", softmax_scale=w.scale)
+    h = hta.hta_create(cfg)
+
+    def accept(i, s):
+        hta.hta_accept(h, lgs[i % R], parent, tokens, target, n, path, bonus, s)
+
+    def accept_commit(i, s):
+        accept(i, s)
+        hta.hta_commit(h, kt, vt, n, path, kc, vc, plens[i], s)
+
+    def timed(fn):
+        s = torch.cuda.current_stream()
+        for i in range(warmup):
+            fn(i, s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(warmup + i, torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    both_ms = timed(accept_commit)
+    status = hta.hta_get_status(h)
+    got = [t.cpu().numpy() for t in (target, n, path, bonus)]
+    last_len = plens[warmup + steps - 1].cpu().numpy()
+    acc_ms = timed(accept)
+    hta.hta_destroy(h)
+    acc_n = int(got[1].sum())
+    accept_bytes = logit_bytes + w.B * w.T * 4 * 4 + w.B * 4 * 2  # logits, parent/tokens/target/path, len/bonus
+    commit_bytes = 2 * 2 * acc_n * w.Hkv * w.D * 2 + w.B * 4 * 3  # K and V rows read + written, lengths
+    gbs = accept_bytes / (acc_ms * 1e-3) / 1e9
+    ok = status == 0 and np.array_equal(last_len, w.prefix_len + 2 * got[1]) and bool((got[1] >= 1).all())
+    row = {
+        "workload": f"accept+commit over {w.B}x{w.T} tree nodes, bf16 logits V={VOCAB}",
+        "us_per_step": round(both_ms * 1e3, 3),
+        "accept_us": round(acc_ms * 1e3, 3),
+        "accepted_tokens": acc_n,
+        "logit_replicas": R,
+        "status_ok_lengths_advanced": ok,
+        "roofline": {
+            "kernel": "argmax_kernel + accept_kernel (hta_accept)",
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic_from_profile(ACCEPT_TRAFFIC_FILE, ACCEPT_SRC),
+            "avg_launch_us": round(acc_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": accept_bytes,
+            "commit_bytes_per_launch": commit_bytes,
+        },
+    }
+    if cpu_seconds > 0:
+        row["cpu_baseline"] = accept_cpu_baseline(case, w, cpu_seconds, accept_bytes)
+    del lgs
+    torch.cuda.synchronize()
+    return row
+
+
+def accept_cpu_baseline(case, w, min_seconds, accept_bytes):
+    """The oracle's accept + commit on the same logits and tree; the commit writes into a
+    cache of room T behind a T-row prefix (its cost does not depend on the prefix)."""
+    import oracle
+    logits = case.logits_f64()
+    kc = np.zeros((w.B, w.Hkv, 2 * w.T, w.D), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    L = np.full(w.B, w.T, dtype=np.int64)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref = oracle.accept(case.parent, case.tree_tokens, logits)
+        oracle.commit(kc, vc, L, w.k_tree, w.v_tree, ref["accept_len"], ref["path"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(dt / reps * 1e6, 1), "unit": "µs per step", "cores": _cores(), "kind": "oracle",
+            "gbs_on_accept_bytes": round(accept_bytes * reps / dt / 1e9, 4),
+            "sample": f"accept over the same {w.B}x{w.T}x{VOCAB} fp64 logits + commit of its rows, "
+                      f"{reps} times, {dt:.2f} s wall"}
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
 
 
 def main():
@@ -238,6 +372,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if not args.no_accept:
+        res["accept_commit"] = accept_commit_row(w, args.steps, args.warmup, args.replica_bytes,
+                                                 0 if args.no_cpu_baseline else args.cpu_seconds / 2)
     print(json.dumps(res), flush=True)
 
 

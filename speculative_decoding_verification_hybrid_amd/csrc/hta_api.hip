@@ -19,6 +19,7 @@ struct hta_handle_s {
   int* err_b;        // [B] bad-tree flags of the last call
   int* status;       // sticky HTA_STATUS_* bits
   unsigned long long* argmax_part;  // [B*T*kArgmaxMaxSplit] partial argmax keys (hta_accept)
+  unsigned* seq_count;              // [B] arrival counters of hta_commit; zero between calls
 };
 
 namespace {
@@ -181,6 +182,8 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   off = align256(off + (size_t)d.B * d.T * hta::kArgmaxMaxSplit * sizeof(unsigned long long));
   const size_t off_eb = off;
   off = align256(off + (size_t)d.B * sizeof(int));
+  const size_t off_ct = off;
+  off = align256(off + (size_t)d.B * sizeof(unsigned));
   const size_t off_st = off;
   off = align256(off + sizeof(int));
   if (hipMalloc(&h->ws, off) != hipSuccess) {
@@ -195,6 +198,7 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   h->err_b = reinterpret_cast<int*>(base + off_eb);
   h->status = reinterpret_cast<int*>(base + off_st);
   h->argmax_part = reinterpret_cast<unsigned long long*>(base + off_ap);
+  h->seq_count = reinterpret_cast<unsigned*>(base + off_ct);
   if (hipMemset(base + off_eb, 0, off - off_eb) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws);
@@ -315,7 +319,8 @@ int hta_commit(hta_handle_t h, const void* k_tree, const void* v_tree, const int
   if (!all_aligned(k_tree, v_tree, static_cast<const void*>(k_cache), static_cast<const void*>(v_cache)))
     return HTA_ERR_INVALID_ARG;
   return check_hip(hta::launch_commit(h->dims, k_tree, v_tree, accept_len, accept_path, k_cache, v_cache,
-                                      prefix_len, h->status, static_cast<hipStream_t>(stream)));
+                                      prefix_len, h->seq_count, h->status,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int hta_get_status(hta_handle_t h, void* stream, int32_t* device_status) {

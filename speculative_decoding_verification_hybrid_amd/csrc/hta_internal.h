@@ -80,13 +80,15 @@ hipError_t launch_clear_status(int* status, hipStream_t s);
 
 // Accept / commit of a verified draft tree (accept.hip). The argmax over the
 // vocabulary splits each logit row over at most kArgmaxMaxSplit workgroups;
-// part holds B*T*kArgmaxMaxSplit keys.
+// part holds B*T*kArgmaxMaxSplit keys. count (B arrival counters of the
+// commit) must be zero before the first call; each call leaves it zero.
 constexpr int kArgmaxMaxSplit = 64;
+int argmax_split_for(int V, bool logits_bf16);
 hipError_t launch_accept(const Dims& d, const void* logits, int V, bool logits_bf16, const int* parent,
                          const int* tree_tokens, unsigned long long* part, int* target_out, int* accept_len,
                          int* accept_path, int* bonus, int* status, hipStream_t s);
 hipError_t launch_commit(const Dims& d, const void* k_tree, const void* v_tree, const int* accept_len,
-                         const int* accept_path, void* k_cache, void* v_cache, int* prefix_len, int* status,
-                         hipStream_t s);
+                         const int* accept_path, void* k_cache, void* v_cache, int* prefix_len, unsigned* count,
+                         int* status, hipStream_t s);
 
 }  // namespace hta
