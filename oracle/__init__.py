@@ -16,3 +16,4 @@ from .hta_oracle import (  # noqa: F401
     verify_attn,
 )
 from .accept_oracle import accept, accept_path, commit, target_tokens  # noqa: F401,E402
+from .draft_oracle import cross_attn, window_append, window_attn, window_visible  # noqa: F401,E402

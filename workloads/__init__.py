@@ -20,3 +20,4 @@ from .gen import (  # noqa: F401
     tree_uniform,
 )
 from .accept_gen import AcceptCase, make_accept_case  # noqa: F401,E402
+from .draft_gen import WindowCase, make_window_case  # noqa: F401,E402
