@@ -20,7 +20,9 @@ roofline (its K launches captured and timed the same way, alone) and the fp64
 CPU oracle's throughput on a bounded sample of the same workload. A second
 leg ("accept_commit") times hta_accept + hta_commit on the same draft tree
 with bf16 target logits over a 128256-token vocabulary, the same way, with
-the oracle's accept + commit on the same inputs beside it.
+the oracle's accept + commit on the same inputs beside it. A third leg
+("draft_cross_attn") times the drafter's cross-attention over the same 32k
+cache with one draft token (hta_cross_attn, the small-row DOT kernel).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --copy-calibration   (adds 8 launches of a plain elementwise
@@ -49,6 +51,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_mfma_llama8b_32k_traffic.t
 PREFIX_SRC = os.path.join(CSRC, "prefix_mfma.hip")
 ACCEPT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "argmax_accept_llama8b_vocab128k_traffic.txt")
 ACCEPT_SRC = os.path.join(CSRC, "accept.hip")
+DOT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_dot_llama8b_draft_32k_traffic.txt")
+DOT_SRC = os.path.join(CSRC, "prefix_dot.hip")
 
 
 def parse():
@@ -62,6 +66,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the CPU oracle baseline")
     ap.add_argument("--no-accept", action="store_true", help="skip the accept + commit leg")
+    ap.add_argument("--no-draft", action="store_true", help="skip the draft cross-attention leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 8 copy-like 256 MiB elementwise kernels before timing")
     return ap.parse_args()
@@ -212,6 +217,114 @@ def accept_commit_row(w, steps, warmup, replica_bytes, cpu_seconds):
     if cpu_seconds > 0:
         row["cpu_baseline"] = accept_cpu_baseline(case, w, cpu_seconds, accept_bytes)
     del lgs
+    torch.cuda.synchronize()
+    return row
+
+
+def draft_cross_row(w, steps, warmup, replica_bytes, cpu_seconds):
+    """The drafter's cross-attention over the target's cache (hta_cross_attn): one draft
+    token per sequence (T = 1) at the same Llama-3.1-8B layer shape and 32k cache, the
+    cache rotated over >= replica_bytes of copies; the split-KV (DOT) kernel alone is
+    timed the same way for its roofline."""
+    import torch
+    from speculative_decoding_verification_hybrid_amd import hta
+    from workloads import make_custom
+
+    L = int(w.prefix_len[0])
+    d = make_custom(B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, Lcap=w.Lcap, T=1, prefix_len=list(w.prefix_len),
+                    dtype="bf16", seed=4321)
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    q, plen = bits(d.q), torch.from_numpy(d.prefix_len).cuda()
+    kv_bytes = 2 * d.Hkv * d.D * int(d.prefix_len.sum()) * 2
+    R = max(1, int(np.ceil(replica_bytes / kv_bytes)))
+    kc0, vc0 = bits(d.k_cache), bits(d.v_cache)
+    kcs = [kc0] + [kc0.clone() for _ in range(R - 1)]
+    vcs = [vc0] + [vc0.clone() for _ in range(R - 1)]
+    out = torch.empty(d.B, d.Hq, 1, d.D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(d.B, d.Hq, 1, dtype=torch.float32, device="cuda")
+    h = hta.hta_create(hta.make_config(batch=d.B, n_q_heads=d.Hq, n_kv_heads=d.Hkv, head_dim=d.D, tree_nodes=1,
+                                       kv_capacity=d.Lcap, dtype="bf16", softmax_scale=d.scale))
+    plan = hta.hta_get_plan(h)
+
+    def timed(fn):
+        s = torch.cuda.current_stream()
+        for i in range(warmup):
+            fn(i, s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(warmup + i, torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    hta.hta_cross_attn(h, q, kc0, vc0, plen, out, lse)
+    torch.cuda.synchronize()
+    out_eager, lse_eager = out.clone(), lse.clone()
+    ms = timed(lambda i, s: hta.hta_cross_attn(h, q, kcs[i % R], vcs[i % R], plen, out, lse, s))
+    same = bool(torch.equal(out, out_eager)) and bool(torch.equal(lse, lse_eager))
+    pms = timed(lambda i, s: hta.hta_prefix_partials(h, q, kcs[i % R], vcs[i % R], plen, s))
+    status = hta.hta_get_status(h)
+    hta.hta_destroy(h)
+    # the drafter's own self-attention: a 512-slot ring (sliding window) plus the new token
+    from workloads import make_window_case
+    wc = make_window_case(B=d.B, Hq=d.Hq, Hkv=d.Hkv, D=d.D, W=512, Tn=1, pos=[L] * d.B, dtype="bf16", seed=99)
+    wt = {n: bits(getattr(wc, n)) for n in ("q", "k_ring", "v_ring", "k_new", "v_new")}
+    wpos = torch.from_numpy(wc.pos).cuda()
+    hw = hta.hta_create(hta.make_config(batch=d.B, n_q_heads=d.Hq, n_kv_heads=d.Hkv, head_dim=d.D, tree_nodes=1,
+                                        kv_capacity=512, dtype="bf16", softmax_scale=d.scale))
+    wms = timed(lambda i, s: hta.hta_window_attn(hw, wt["q"], wt["k_ring"], wt["v_ring"], wt["k_new"], wt["v_new"],
+                                                 wpos, out, lse, s))
+    ams = timed(lambda i, s: hta.hta_window_append(hw, wt["k_new"], wt["v_new"], wt["k_ring"], wt["v_ring"],
+                                                   wpos, s))
+    status |= hta.hta_get_status(hw)
+    hta.hta_destroy(hw)
+    gbs = kv_bytes / (pms * 1e-3) / 1e9
+    row = {
+        "workload": f"draft cross-attention, {d.Hq} q / {d.Hkv} kv heads, D {d.D}, 1 draft token, {L}-token cache",
+        "us_per_call": round(ms * 1e3, 3),
+        "tokens_per_s": round(d.B / (ms * 1e-3), 1),
+        "window_attn_us": round(wms * 1e3, 3),
+        "window_append_us": round(ams * 1e3, 3),
+        "window": "512-slot ring, 1 new token (hta_window_attn, hta_window_append)",
+        "path": plan["path"],
+        "num_workgroups": plan["num_workgroups"],
+        "kv_replicas": R,
+        "outputs_match_eager_status_ok": same and status == 0,
+        "roofline": {
+            "kernel": "prefix_dot_kernel<4> (split-KV, v_dot2; hta_prefix_partials)",
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic_from_profile(DOT_TRAFFIC_FILE, DOT_SRC),
+            "avg_launch_us": round(pms * 1e3, 3),
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+    if cpu_seconds > 0:
+        import oracle
+        args = [d.as_f64(n) for n in ("q", "k_cache", "v_cache")]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.cross_attn(*args, d.prefix_len, d.scale)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= cpu_seconds:
+                break
+        row["cpu_baseline"] = {"value": round(kv_bytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": _cores(),
+                               "kind": "oracle", "us_per_call": round(dt / reps * 1e6, 1),
+                               "sample": f"the whole call (all {d.Hq} heads, {L}-token cache) {reps} times, "
+                                         f"{dt:.2f} s wall"}
+    del kcs, vcs
     torch.cuda.synchronize()
     return row
 
@@ -372,6 +485,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if not args.no_draft:
+        res["draft_cross_attn"] = draft_cross_row(w, args.steps, args.warmup, args.replica_bytes,
+                                                  0 if args.no_cpu_baseline else args.cpu_seconds / 4)
     if not args.no_accept:
         res["accept_commit"] = accept_commit_row(w, args.steps, args.warmup, args.replica_bytes,
                                                  0 if args.no_cpu_baseline else args.cpu_seconds / 2)

@@ -93,8 +93,11 @@ enum hta_device_status {
   HTA_STATUS_BAD_PATH = 8         /* hta_commit: an accept_path entry outside [0, T) */
 };
 
-/* Prefix-kernel implementation (see hta_plan_t.path). */
-enum hta_path { HTA_PATH_AUTO = 0, HTA_PATH_MFMA = 1, HTA_PATH_VALU = 2 };
+/* Prefix-kernel implementation (see hta_plan_t.path). MFMA: bf16 with
+ * G*T >= 16 query rows per KV head (32-row matrix-core blocks). DOT: bf16,
+ * D = 128, G*T <= 8 (dot products on the vector ALUs, cross-lane reductions;
+ * the drafter's cross-attention shape). VALU: float32, and everything else. */
+enum hta_path { HTA_PATH_AUTO = 0, HTA_PATH_MFMA = 1, HTA_PATH_VALU = 2, HTA_PATH_DOT = 3 };
 
 typedef struct {
   int32_t batch;          /* B >= 1 */
@@ -106,12 +109,13 @@ typedef struct {
   int32_t dtype;          /* enum hta_dtype */
   float softmax_scale;    /* <= 0 selects 1/sqrt(D) */
   int32_t num_workgroups; /* prefix-kernel workgroups; 0 = sized from the device */
-  int32_t force_path;     /* enum hta_path; AUTO picks MFMA for bf16 with G*T >= 16 */
+  int32_t force_path;     /* enum hta_path; AUTO picks MFMA for bf16 with G*T >= 16, DOT for
+                             bf16 with D = 128 and G*T <= 8, else VALU */
   int32_t qblocks_per_wave; /* MFMA path: 32-row query blocks per wave, 1 or 2; 0 = planned */
 } hta_config_t;
 
 typedef struct {
-  int32_t path;                /* HTA_PATH_MFMA or HTA_PATH_VALU */
+  int32_t path;                /* HTA_PATH_MFMA, HTA_PATH_VALU or HTA_PATH_DOT */
   int32_t num_workgroups;      /* workgroups per row group of the prefix kernel */
   int32_t row_groups;          /* prefix-kernel grid.y: row groups per KV head */
   int32_t rows_per_group;      /* query rows (of G*T per KV head) per row group */
@@ -146,6 +150,43 @@ HTA_API int hta_get_plan(hta_handle_t h, hta_plan_t* plan);
 HTA_API int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
                     const void* k_tree, const void* v_tree, const int32_t* parent,
                     const int32_t* prefix_len, void* out, float* lse, void* stream);
+
+/* The drafter's cross-attention over the target model's KV cache: every
+ * query row attends, with no mask, to the first prefix_len[b] positions of
+ * its KV head (LongSpec summary pages, §2.A "memory-efficient architecture":
+ * the draft model reads the cache the target keeps anyway). q [B,Hq,T,D]
+ * with T = the handle's tree_nodes (draft query tokens per sequence), caches
+ * [B,Hkv,Lcap,D]; out [B,Hq,T,D] in the handle's dtype, lse [B,Hq,T] float32
+ * natural log. A sequence with prefix_len 0 gets out = 0 and lse = -inf; a
+ * prefix_len outside [0, Lcap] gives NaN rows + HTA_STATUS_BAD_PREFIX.
+ * bf16 handles with G*T <= 8 run the DOT kernel. Same split-KV kernel and
+ * merge as hta_verify_attn, without the tree tile. Pointers as there. */
+HTA_API int hta_cross_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* prefix_len, void* out, float* lse, void* stream);
+
+/* The drafter's sliding-window self-attention (LongSpec summary pages, §2.A
+ * "memory-efficient architecture": a window of 512 positions keeps the draft
+ * model's cache at a fixed size). The handle's kv_capacity is the window W
+ * and its tree_nodes the number Tn <= W of new tokens per step. The draft
+ * cache is a ring, k_ring/v_ring [B,Hkv,W,D], slot = position mod W; pos[b]
+ * (int32, device) counts the positions written before this step, so the ring
+ * holds positions max(0, pos-W) .. pos-1 (slots not yet written are never
+ * read and may hold anything). k_new/v_new [B,Hkv,Tn,D] are the new tokens
+ * at positions pos .. pos+Tn-1; q [B,Hq,Tn,D]. New token j attends to the
+ * positions max(0, pos+j-W+1) .. pos+j, its own included. out [B,Hq,Tn,D] in
+ * the handle's dtype, lse [B,Hq,Tn] float32 natural log. A negative pos[b]
+ * gives NaN rows + HTA_STATUS_BAD_PREFIX. Returns HTA_ERR_UNSUPPORTED when
+ * Tn > W. Pointers 16-byte aligned. */
+HTA_API int hta_window_attn(hta_handle_t h, const void* q, const void* k_ring, const void* v_ring,
+                            const void* k_new, const void* v_new, const int32_t* pos, void* out, float* lse,
+                            void* stream);
+
+/* Writes the Tn new tokens into the ring (new token j to slot (pos+j) mod W)
+ * and advances pos by Tn, on the stream. A negative pos[b] leaves that
+ * sequence unchanged and sets HTA_STATUS_BAD_PREFIX. Calls on one handle must
+ * not overlap (they share arrival counters with hta_commit). Tn <= W. */
+HTA_API int hta_window_append(hta_handle_t h, const void* k_new, const void* v_new, void* k_ring, void* v_ring,
+                              int32_t* pos, void* stream);
 
 /* The tree mask alone: mask_out[b][i] (uint64, device) has bit j set iff
  * tree node j is node i or one of its ancestors. A sequence whose parent

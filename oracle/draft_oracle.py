@@ -58,7 +58,9 @@ def cross_attn(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, prefix_l
 
 
 def window_visible(P: int, W: int, Tn: int) -> np.ndarray:
-    """Boolean [Tn, W + Tn]: which ring slots and which new tokens new token j sees."""
+    """Boolean [Tn, W + Tn]: which ring slots and which new tokens new token j sees (Tn <= W)."""
+    if Tn > W:
+        raise ValueError("more new tokens than the window holds")
     vis = np.zeros((Tn, W + Tn), dtype=bool)
     for j in range(Tn):
         t = P + j  # absolute position of new token j

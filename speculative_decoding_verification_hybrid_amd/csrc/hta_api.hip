@@ -43,11 +43,15 @@ int validate(const hta_config_t* c) {
   if (c->n_q_heads % c->n_kv_heads != 0) return HTA_ERR_INVALID_ARG;
   if (c->dtype != HTA_F32 && c->dtype != HTA_BF16) return HTA_ERR_INVALID_ARG;
   if (c->num_workgroups < 0) return HTA_ERR_INVALID_ARG;
-  if (c->force_path < HTA_PATH_AUTO || c->force_path > HTA_PATH_VALU) return HTA_ERR_INVALID_ARG;
+  if (c->force_path < HTA_PATH_AUTO || c->force_path > HTA_PATH_DOT) return HTA_ERR_INVALID_ARG;
   if (!(c->softmax_scale == c->softmax_scale)) return HTA_ERR_INVALID_ARG;  // NaN
   if (c->head_dim != 64 && c->head_dim != 128) return HTA_ERR_UNSUPPORTED;
   if (c->tree_nodes > 64) return HTA_ERR_UNSUPPORTED;
   if (c->force_path == HTA_PATH_MFMA && c->dtype != HTA_BF16) return HTA_ERR_UNSUPPORTED;
+  if (c->force_path == HTA_PATH_DOT &&
+      !hta::prefix_dot_supported(c->head_dim, (c->n_q_heads / c->n_kv_heads) * c->tree_nodes,
+                                 c->dtype == HTA_BF16))
+    return HTA_ERR_UNSUPPORTED;
   if (c->qblocks_per_wave < 0 || c->qblocks_per_wave > 2) return HTA_ERR_INVALID_ARG;
   // Index arithmetic limits: rows and per-sequence KV spans stay within int32.
   const int64_t rows = (int64_t)c->batch * c->n_q_heads * c->tree_nodes;
@@ -63,7 +67,8 @@ int validate(const hta_config_t* c) {
 // (grid.y). The plan takes qb = 1: with a single wave per SIMD the two-block
 // kernel's instruction issue (its LDS reads in particular) is not hidden, and
 // it measures slower at the shapes benchmarked; qb = 2 is taken on request.
-// VALU path: 16 rows per workgroup.
+// VALU path: 16 rows per workgroup. DOT path: all M <= 8 rows in one
+// workgroup of 4 waves.
 void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) {
   pl->path = path;
   if (path == HTA_PATH_MFMA) {
@@ -77,6 +82,11 @@ void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) 
     pl->rows_per_group = per * 32 * qb;
     pl->waves = per;
     pl->qb = qb;
+  } else if (path == HTA_PATH_DOT) {
+    pl->row_groups = 1;
+    pl->rows_per_group = d.M;
+    pl->waves = 4;
+    pl->qb = 0;
   } else {
     pl->row_groups = (d.M + 15) / 16;
     pl->rows_per_group = 16;
@@ -96,6 +106,8 @@ void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) 
 static int launch_split(hta_handle_t h, const hta::PrefixInputs& in, hipStream_t s) {
   if (h->pl.path == HTA_PATH_MFMA)
     return check_hip(hta::launch_prefix_mfma(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
+  if (h->pl.path == HTA_PATH_DOT)
+    return check_hip(hta::launch_prefix_dot(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
   return check_hip(hta::launch_prefix_valu(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
 }
 
@@ -144,14 +156,18 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   d.scale_log2 = scale * hta::kLog2e;
 
   int path = cfg->force_path;
-  if (path == HTA_PATH_AUTO) path = (d.bf16 && d.M >= 16) ? HTA_PATH_MFMA : HTA_PATH_VALU;
+  if (path == HTA_PATH_AUTO)
+    path = (d.bf16 && d.M >= 16)                         ? HTA_PATH_MFMA
+           : hta::prefix_dot_supported(d.D, d.M, d.bf16) ? HTA_PATH_DOT
+                                                         : HTA_PATH_VALU;
   plan_rows(d, path, cfg->qblocks_per_wave, &h->pl);
   if (path == HTA_PATH_MFMA && !hta::prefix_mfma_supported(d.D, h->pl.waves, h->pl.qb)) {
     delete h;
     return HTA_ERR_UNSUPPORTED;
   }
-  const int occ = path == HTA_PATH_MFMA ? hta::prefix_mfma_occupancy(d.D, h->pl.waves, h->pl.qb)
-                                        : hta::prefix_valu_occupancy(d.D, d.bf16);
+  const int occ = path == HTA_PATH_MFMA  ? hta::prefix_mfma_occupancy(d.D, h->pl.waves, h->pl.qb)
+                  : path == HTA_PATH_DOT ? hta::prefix_dot_occupancy(d.M)
+                                         : hta::prefix_valu_occupancy(d.D, d.bf16);
   int64_t nwg = cfg->num_workgroups;
   if (nwg <= 0) {
     nwg = (int64_t)cus * (occ > 0 ? occ : 1) / h->pl.row_groups;
@@ -251,6 +267,36 @@ int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const vo
   HTA_TRY(launch_split(h, in, s));
   return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, 1, prefix_len, h->slots, h->err_b, out,
                                            h->dims.bf16, lse, h->status, s));
+}
+
+int hta_cross_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* prefix_len, void* out, float* lse, void* stream) {
+  if (!h || !q || !k_cache || !v_cache || !prefix_len || !out || !lse) return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(q, k_cache, v_cache, out)) return HTA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hta::PrefixInputs in = {q, k_cache, v_cache, nullptr, nullptr, nullptr, prefix_len};
+  HTA_TRY(launch_split(h, in, s));
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, 0, prefix_len, h->slots, nullptr, out,
+                                           h->dims.bf16, lse, h->status, s));
+}
+
+int hta_window_attn(hta_handle_t h, const void* q, const void* k_ring, const void* v_ring, const void* k_new,
+                    const void* v_new, const int32_t* pos, void* out, float* lse, void* stream) {
+  if (!h || !q || !k_ring || !v_ring || !k_new || !v_new || !pos || !out || !lse) return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(q, k_ring, v_ring, k_new, v_new, out)) return HTA_ERR_INVALID_ARG;
+  if (h->dims.T > h->dims.Lcap) return HTA_ERR_UNSUPPORTED;  // more new tokens than the window holds
+  return check_hip(hta::launch_window_attn(h->dims, q, k_ring, v_ring, k_new, v_new, pos, out, lse, h->status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int hta_window_append(hta_handle_t h, const void* k_new, const void* v_new, void* k_ring, void* v_ring,
+                      int32_t* pos, void* stream) {
+  if (!h || !k_new || !v_new || !k_ring || !v_ring || !pos) return HTA_ERR_INVALID_ARG;
+  if (!all_aligned(k_new, v_new, static_cast<const void*>(k_ring), static_cast<const void*>(v_ring)))
+    return HTA_ERR_INVALID_ARG;
+  if (h->dims.T > h->dims.Lcap) return HTA_ERR_UNSUPPORTED;
+  return check_hip(hta::launch_window_append(h->dims, k_new, v_new, k_ring, v_ring, pos, h->seq_count, h->status,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int hta_tree_mask(hta_handle_t h, const int32_t* parent, uint64_t* mask_out, void* stream) {

@@ -53,6 +53,21 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
                               int* err_b, int* status, hipStream_t s);
 hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                               int* err_b, int* status, hipStream_t s);
+// Small-M bf16 split-KV kernel (v_dot2 + DPP; D = 128, at most kDotMaxRows
+// query rows per KV head). Float slots, same split and tree fusion.
+constexpr int kDotMaxRows = 8;
+hipError_t launch_prefix_dot(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
+                             int* err_b, int* status, hipStream_t s);
+bool prefix_dot_supported(int D, int M, bool bf16);
+int prefix_dot_occupancy(int M);
+// The drafter's sliding-window self-attention over a ring of W = Lcap slots
+// with T new tokens (window.hip), and the append of the new tokens to the
+// ring (count: the B arrival counters shared with the commit).
+hipError_t launch_window_attn(const Dims& d, const void* q, const void* k_ring, const void* v_ring,
+                              const void* k_new, const void* v_new, const int* pos, void* out, float* lse,
+                              int* status, hipStream_t s);
+hipError_t launch_window_append(const Dims& d, const void* k_new, const void* v_new, void* k_ring, void* v_ring,
+                                int* pos, unsigned* count, int* status, hipStream_t s);
 // Occupancy (workgroups per CU) of the chosen prefix kernel, for sizing nwg.
 int prefix_mfma_occupancy(int D, int waves, int qb);
 int prefix_valu_occupancy(int D, bool bf16);

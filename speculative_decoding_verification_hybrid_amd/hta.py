@@ -40,6 +40,7 @@ HTA_STATUS_BAD_PATH = 8
 HTA_PATH_AUTO = 0
 HTA_PATH_MFMA = 1
 HTA_PATH_VALU = 2
+HTA_PATH_DOT = 3
 
 
 class HtaError(RuntimeError):
@@ -91,6 +92,9 @@ _SIGNATURES = {
     "hta_tree_mask": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
     "hta_tree_attn": (ctypes.c_int, [_vp] * 7 + [_vp]),
     "hta_prefix_attn": (ctypes.c_int, [_vp] * 7 + [_vp]),
+    "hta_cross_attn": (ctypes.c_int, [_vp] * 7 + [_vp]),
+    "hta_window_attn": (ctypes.c_int, [_vp] * 9 + [_vp]),
+    "hta_window_append": (ctypes.c_int, [_vp] * 6 + [_vp]),
     "hta_prefix_partials": (ctypes.c_int, [_vp] * 5 + [_vp]),
     "hta_merge_prefix": (ctypes.c_int, [_vp] * 4 + [_vp]),
     "hta_lse_merge": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -263,6 +267,57 @@ def hta_tree_attn(h: Handle, q, k_tree, v_tree, parent, o_tree, lse_tree, stream
     ]
     _check(load_library().hta_tree_attn(_vp(h.ptr), *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
            "hta_tree_attn")
+
+
+def hta_cross_attn(h: Handle, q, k_cache, v_cache, prefix_len, out, lse, stream=None) -> None:
+    """The drafter's cross-attention over the target's cache; out in the handle's dtype."""
+    import torch
+    B, Hq, Hkv, D, T, Lcap = h.dims
+    dt = _io_dtype(h)
+    args = [
+        _tensor(q, "q", dt, (B, Hq, T, D)),
+        _tensor(k_cache, "k_cache", dt, (B, Hkv, Lcap, D)),
+        _tensor(v_cache, "v_cache", dt, (B, Hkv, Lcap, D)),
+        _tensor(prefix_len, "prefix_len", torch.int32, (B,)),
+        _tensor(out, "out", dt, (B, Hq, T, D)),
+        _tensor(lse, "lse", torch.float32, (B, Hq, T)),
+    ]
+    _check(load_library().hta_cross_attn(_vp(h.ptr), *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
+           "hta_cross_attn")
+
+
+def hta_window_attn(h: Handle, q, k_ring, v_ring, k_new, v_new, pos, out, lse, stream=None) -> None:
+    """Sliding-window self-attention of the drafter: ring of W = kv_capacity slots, Tn = tree_nodes new tokens."""
+    import torch
+    B, Hq, Hkv, D, T, W = h.dims
+    dt = _io_dtype(h)
+    args = [
+        _tensor(q, "q", dt, (B, Hq, T, D)),
+        _tensor(k_ring, "k_ring", dt, (B, Hkv, W, D)),
+        _tensor(v_ring, "v_ring", dt, (B, Hkv, W, D)),
+        _tensor(k_new, "k_new", dt, (B, Hkv, T, D)),
+        _tensor(v_new, "v_new", dt, (B, Hkv, T, D)),
+        _tensor(pos, "pos", torch.int32, (B,)),
+        _tensor(out, "out", dt, (B, Hq, T, D)),
+        _tensor(lse, "lse", torch.float32, (B, Hq, T)),
+    ]
+    _check(load_library().hta_window_attn(_vp(h.ptr), *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
+           "hta_window_attn")
+
+
+def hta_window_append(h: Handle, k_new, v_new, k_ring, v_ring, pos, stream=None) -> None:
+    import torch
+    B, Hq, Hkv, D, T, W = h.dims
+    dt = _io_dtype(h)
+    args = [
+        _tensor(k_new, "k_new", dt, (B, Hkv, T, D)),
+        _tensor(v_new, "v_new", dt, (B, Hkv, T, D)),
+        _tensor(k_ring, "k_ring", dt, (B, Hkv, W, D)),
+        _tensor(v_ring, "v_ring", dt, (B, Hkv, W, D)),
+        _tensor(pos, "pos", torch.int32, (B,)),
+    ]
+    _check(load_library().hta_window_append(_vp(h.ptr), *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
+           "hta_window_append")
 
 
 def hta_prefix_attn(h: Handle, q, k_cache, v_cache, prefix_len, o_prefix, lse_prefix, stream=None) -> None:

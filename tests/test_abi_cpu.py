@@ -63,7 +63,11 @@ def test_named_workloads_validate(lib, key):
     (dict(head_dim=256), hta.HTA_ERR_UNSUPPORTED),
     (dict(tree_nodes=65), hta.HTA_ERR_UNSUPPORTED),
     (dict(num_workgroups=-1), hta.HTA_ERR_INVALID_ARG),
-    (dict(force_path=3), hta.HTA_ERR_INVALID_ARG),
+    (dict(force_path=4), hta.HTA_ERR_INVALID_ARG),
+    (dict(force_path=hta.HTA_PATH_DOT), hta.HTA_ERR_UNSUPPORTED),                    # 4 x 64 rows > 8
+    (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2), hta.HTA_OK),                  # 4 x 2 rows
+    (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2, dtype="f32"), hta.HTA_ERR_UNSUPPORTED),
+    (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2, head_dim=64), hta.HTA_ERR_UNSUPPORTED),
     (dict(force_path=hta.HTA_PATH_MFMA, dtype="f32"), hta.HTA_ERR_UNSUPPORTED),
     (dict(softmax_scale=math.nan), hta.HTA_ERR_INVALID_ARG),
     (dict(kv_capacity=1 << 30), hta.HTA_ERR_UNSUPPORTED),
@@ -103,6 +107,9 @@ def test_null_arguments_fail_before_any_hip_call(lib):
     assert lib.hta_get_status(None, None, None) == hta.HTA_ERR_INVALID_ARG
     assert lib.hta_accept(None, None, 100, hta.HTA_BF16, *([None] * 7)) == hta.HTA_ERR_INVALID_ARG
     assert lib.hta_commit(None, *([None] * 8)) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_cross_attn(None, *([None] * 7)) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_window_attn(None, *([None] * 9)) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_window_append(None, *([None] * 6)) == hta.HTA_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

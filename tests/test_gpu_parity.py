@@ -119,7 +119,9 @@ EDGE = {
     "m160_five_waves": dict(B=2, Hq=10, Hkv=2, D=128, Lcap=1100, T=32, prefix_len=[1100, 613]),
     "m512_two_row_groups": dict(B=1, Hq=16, Hkv=2, D=128, Lcap=640, T=64, prefix_len=[640]),
     "m224_seven_waves": dict(B=1, Hq=14, Hkv=2, D=128, Lcap=600, T=32, prefix_len=[599]),
-    "bf16_small_rows_valu": dict(B=2, Hq=4, Hkv=4, D=128, Lcap=500, T=8, prefix_len=[500, 77]),
+    "bf16_small_rows_dot": dict(B=2, Hq=4, Hkv=4, D=128, Lcap=500, T=8, prefix_len=[500, 77]),
+    "bf16_small_rows_forced_valu": dict(B=2, Hq=4, Hkv=4, D=128, Lcap=500, T=8, prefix_len=[500, 77],
+                                        cfg=dict(force_path=hta.HTA_PATH_VALU)),
     "bf16_forced_valu": dict(B=1, Hq=8, Hkv=2, D=128, Lcap=400, T=16, prefix_len=[390],
                              cfg=dict(force_path=hta.HTA_PATH_VALU)),
     "f32_ragged": dict(B=3, Hq=4, Hkv=2, D=64, Lcap=300, T=8, prefix_len=[300, 129, 0], dtype="f32"),
