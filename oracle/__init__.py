@@ -17,3 +17,4 @@ from .hta_oracle import (  # noqa: F401
 )
 from .accept_oracle import accept, accept_path, commit, target_tokens  # noqa: F401,E402
 from .draft_oracle import cross_attn, window_append, window_attn, window_visible  # noqa: F401,E402
+from .tree_oracle import build_tree, build_trees, most_recent_match, ranked_tokens  # noqa: F401,E402

@@ -1,0 +1,118 @@
+"""Pins of the tree-construction oracle (CPU only).
+
+The ranking is checked against a plain repeated-maximum loop, the n-gram
+search against a forward scan that keeps the last hit, the whole construction
+against a hand-worked example (tests/golden/tree_hand_example.json) and
+against structural invariants; two planted mistakes must fail the example.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import tree_oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tree_hand_example.json")
+
+
+def _loop_ranking(v, n):
+    left = list(range(len(v)))
+    out = []
+    for _ in range(n):
+        best = left[0]
+        for i in left[1:]:
+            if v[i] > v[best]:  # strict: an equal later value does not win
+                best = i
+        out.append(best)
+        left.remove(best)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ranking_matches_repeated_maximum(seed):
+    rng = np.random.default_rng(seed)
+    v = np.round(rng.standard_normal(50) * 2) / 2  # many ties
+    assert oracle.ranked_tokens(v, 12) == _loop_ranking(list(v), 12)
+
+
+def _forward_last_match(seq, gram, before):
+    m, last = len(gram), -1
+    for p in range(m - 1, min(before, len(seq))):
+        if list(seq[p - m + 1:p + 1]) == list(gram):
+            last = p
+    return last
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_most_recent_match_matches_forward_scan(seed):
+    rng = np.random.default_rng(100 + seed)
+    seq = list(rng.integers(0, 4, size=80))
+    for m in (1, 2, 3, 4):
+        for _ in range(20):
+            gram = list(rng.integers(0, 4, size=m))
+            before = int(rng.integers(0, 81))
+            assert oracle.most_recent_match(seq, gram, before) == _forward_last_match(seq, gram, before)
+
+
+def _golden_inputs(g):
+    logits = np.zeros(g["vocab"])
+    for t, val in g["logits_nonzero"].items():
+        logits[int(t)] = val
+    return g["history"], logits
+
+
+def test_hand_example():
+    g = json.load(open(GOLDEN))
+    hist, logits = _golden_inputs(g)
+    tok, par, n = oracle.build_tree(hist, logits, g["k"], g["m"], g["keep_first"], g["keep"], g["T"])
+    assert list(tok) == g["tokens"] and list(par) == g["parent"] and n == g["n_nodes"]
+
+
+def test_planted_mistakes_fail_the_hand_example(monkeypatch):
+    g = json.load(open(GOLDEN))
+    hist, logits = _golden_inputs(g)
+    args = (hist, logits, g["k"], g["m"], g["keep_first"], g["keep"], g["T"])
+    good = oracle.build_tree(*args)
+    real = tree_oracle.most_recent_match
+    # (1) query 1 allowed to match itself (its own end, the last position)
+    monkeypatch.setattr(tree_oracle, "most_recent_match", lambda s, gr, before: real(s, gr, len(s)))
+    bad = tree_oracle.build_tree(*args)
+    assert list(bad[0]) != list(good[0])
+    # (2) retrieved tokens start at the match's last token instead of after it
+    monkeypatch.setattr(tree_oracle, "most_recent_match", lambda s, gr, before: max(-1, real(s, gr, before) - 1)
+                        if real(s, gr, before) >= 0 else -1)
+    bad = tree_oracle.build_tree(*args)
+    assert list(bad[0]) != list(good[0])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_structure_and_truncation(seed):
+    rng = np.random.default_rng(200 + seed)
+    hist = list(rng.integers(0, 6, size=int(rng.integers(1, 120))))
+    logits = rng.standard_normal(6 + 20)
+    k, m = int(rng.integers(1, 8)), int(rng.integers(1, 5))
+    keep = sorted(rng.integers(0, 6, size=k).tolist(), reverse=True)
+    kf = int(rng.integers(0, 6))
+    tok, par, n = oracle.build_tree(hist, logits, k, m, kf, keep, 64)
+    seq = hist + [int(tok[0])]
+    assert par[0] == -1 and all(0 <= par[i] < i for i in range(1, 64))
+    assert n <= 1 + kf + k + sum(keep)
+    assert all(tok[i] == -1 and par[i] == 0 for i in range(n, 64))
+    # the guesses are the children of the root that are not on query 1's chain
+    ranked = oracle.ranked_tokens(logits, k + 1)
+    assert tok[0] == ranked[0]
+    root_kids = [i for i in range(1, n) if par[i] == 0]
+    chain1 = 1 if (n > 1 and par[1] == 0 and (len(root_kids) > k)) else 0
+    assert [int(tok[i]) for i in root_kids[chain1:]] == ranked[1:1 + len(root_kids) - chain1]
+    # every retrieved chain is a run of consecutive tokens of the sequence
+    for i in range(1, n):
+        kids = [c for c in range(n) if par[c] == i]
+        assert len(kids) <= 1
+    # a smaller tree is a prefix of the larger one
+    for T in (1, 2, 5, 17):
+        t2, p2, n2 = oracle.build_tree(hist, logits, k, m, kf, keep, T)
+        assert list(t2[:min(T, n)]) == list(tok[:min(T, n)]) and n2 == min(T, n)
+        assert list(p2[:n2]) == list(par[:n2])
