@@ -22,7 +22,9 @@ leg ("accept_commit") times hta_accept + hta_commit on the same draft tree
 with bf16 target logits over a 128256-token vocabulary, the same way, with
 the oracle's accept + commit on the same inputs beside it. A third leg
 ("draft_cross_attn") times the drafter's cross-attention over the same 32k
-cache with one draft token (hta_cross_attn, the small-row DOT kernel).
+cache with one draft token (hta_cross_attn, the small-row DOT kernel), and a
+fourth ("tree_build") the construction of the next draft tree from the last
+logits and a 32k-token history (hta_build_tree).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --copy-calibration   (adds 8 launches of a plain elementwise
@@ -67,6 +69,7 @@ def parse():
                     help="minimum wall time of the CPU oracle baseline")
     ap.add_argument("--no-accept", action="store_true", help="skip the accept + commit leg")
     ap.add_argument("--no-draft", action="store_true", help="skip the draft cross-attention leg")
+    ap.add_argument("--no-tree", action="store_true", help="skip the tree-construction leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 8 copy-like 256 MiB elementwise kernels before timing")
     return ap.parse_args()
@@ -329,6 +332,75 @@ def draft_cross_row(w, steps, warmup, replica_bytes, cpu_seconds):
     return row
 
 
+TREE_KEEP = [8, 6, 5, 4, 4, 3, 3, 2, 2, 2, 1, 1, 1, 1, 1]  # tokens kept per guess rank (non-increasing)
+
+
+def tree_build_row(w, steps, warmup, cpu_seconds):
+    """hta_build_tree for one sequence: the last logits over the Llama-3.1-8B vocabulary
+    (bf16), a 32k-token history, 15 next-next guesses, 3-grams, a 64-node tree. The
+    inputs are a few hundred KB, so they stay in the caches: the figure is the call's
+    latency, not a stream."""
+    import torch
+    from speculative_decoding_verification_hybrid_amd import hta
+    from workloads import make_tree_case
+
+    cap = int(w.prefix_len[0])
+    case = make_tree_case(B=1, V=VOCAB, cap=cap, history_len=[cap], alphabet=40, seed=7)
+    lg = torch.from_numpy(case.logits.view(np.int16)).view(torch.bfloat16).cuda()
+    hist = torch.from_numpy(case.history).cuda()
+    hl = torch.from_numpy(case.history_len).cuda()
+    tok = torch.empty(1, w.T, dtype=torch.int32, device="cuda")
+    par = torch.empty(1, w.T, dtype=torch.int32, device="cuda")
+    nn = torch.empty(1, dtype=torch.int32, device="cuda")
+    k, m, kf = len(TREE_KEEP), 3, 8
+    params = hta.make_tree_params(k, m, kf, TREE_KEEP)
+    h = hta.hta_create(hta.make_config(batch=1, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, tree_nodes=w.T,
+                                       kv_capacity=w.Lcap))
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        hta.hta_build_tree(h, lg, hist, hl, params, tok, par, nn, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            hta.hta_build_tree(h, lg, hist, hl, params, tok, par, nn, torch.cuda.current_stream())
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream()
+    e0.record(s)
+    g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    status = hta.hta_get_status(h)
+    hta.hta_destroy(h)
+    nbytes = VOCAB * 2 + cap * 4 + w.T * 8 + 4
+    row = {
+        "workload": f"tree construction: bf16 logits V={VOCAB}, {cap}-token history, k={k} guesses, {m}-grams, "
+                    f"{w.T}-node tree",
+        "us_per_call": round(ms * 1e3, 3),
+        "n_nodes": int(nn.item()),
+        "status_ok": status == 0,
+        "bytes_per_call": nbytes,
+        "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+    }
+    if cpu_seconds > 0:
+        import oracle
+        lf = case.logits_f64()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.build_trees(case.history, case.history_len, lf, k, m, kf, TREE_KEEP, w.T)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= cpu_seconds:
+                break
+        row["cpu_baseline"] = {"value": round(dt / reps * 1e6, 1), "unit": "µs per call", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the same call {reps} times, {dt:.2f} s wall (pure Python search)"}
+    return row
+
+
 def accept_cpu_baseline(case, w, min_seconds, accept_bytes):
     """The oracle's accept + commit on the same logits and tree; the commit writes into a
     cache of room T behind a T-row prefix (its cost does not depend on the prefix)."""
@@ -488,6 +560,9 @@ def main():
     if not args.no_draft:
         res["draft_cross_attn"] = draft_cross_row(w, args.steps, args.warmup, args.replica_bytes,
                                                   0 if args.no_cpu_baseline else args.cpu_seconds / 4)
+    if not args.no_tree:
+        res["tree_build"] = tree_build_row(w, args.steps, args.warmup,
+                                           0 if args.no_cpu_baseline else args.cpu_seconds / 4)
     if not args.no_accept:
         res["accept_commit"] = accept_commit_row(w, args.steps, args.warmup, args.replica_bytes,
                                                  0 if args.no_cpu_baseline else args.cpu_seconds / 2)

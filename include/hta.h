@@ -188,6 +188,41 @@ HTA_API int hta_window_attn(hta_handle_t h, const void* q, const void* k_ring, c
 HTA_API int hta_window_append(hta_handle_t h, const void* k_new, const void* v_new, void* k_ring, void* v_ring,
                               int32_t* pos, void* stream);
 
+/* Draft-tree construction (LogitSpec summary pages, §2 "LogitSpec workflow":
+ * next token, top-k next-next guesses without it, dual n-gram retrieval,
+ * rank-based pruning). */
+#define HTA_MAX_TREE_GUESSES 31
+#define HTA_MAX_NGRAM 8
+typedef struct {
+  int32_t k;          /* next-next guesses: 0 .. HTA_MAX_TREE_GUESSES */
+  int32_t m;          /* n-gram length of both queries: 1 .. HTA_MAX_NGRAM */
+  int32_t keep_first; /* tokens kept after query 1's match: 0 .. 64 */
+  int32_t keep[HTA_MAX_TREE_GUESSES]; /* tokens kept after the match for the guess of rank r: 0 .. 64 */
+} hta_tree_params_t;
+
+/* Builds one draft tree per sequence from its last logits and its own tokens.
+ * logits [B,V] (the last position's, float32 or bfloat16 per logits_dtype,
+ * V = vocab <= 262144 and >= k+1); history [B,history_cap] int32 token ids
+ * >= 0 with history_len[b] (0 .. history_cap) valid entries, the last being
+ * the current token; params is a host pointer. x1 = the largest logit (lowest
+ * index on ties); guesses = the next k in that order. The sequence searched is
+ * history followed by x1. Query 1 = its last m tokens; query 2 for guess g =
+ * its last m-1 tokens followed by g; a match is the most recent earlier
+ * occurrence (query 1 never matches itself) and the tokens after it are
+ * retrieved. Output (T = the handle's tree_nodes): node 0 = x1 (parent -1);
+ * then up to keep_first tokens retrieved for query 1, a chain under node 0;
+ * then for each guess by rank r a node under node 0 and up to keep[r]
+ * retrieved tokens chained under it; nodes past T are dropped in that order.
+ * tree_tokens [B,T], parent [B,T] (a valid parent array for hta_verify_attn),
+ * n_nodes [B] = nodes used; unused slots hold token -1 under node 0. A
+ * history_len outside [0, history_cap] gives n_nodes 0, all tokens -1 and
+ * HTA_STATUS_BAD_PREFIX. Returns HTA_ERR_INVALID_ARG for parameters outside
+ * the ranges above, HTA_ERR_UNSUPPORTED for a larger vocabulary. */
+HTA_API int hta_build_tree(hta_handle_t h, const void* logits, int32_t vocab, int32_t logits_dtype,
+                           const int32_t* history, int32_t history_cap, const int32_t* history_len,
+                           const hta_tree_params_t* params, int32_t* tree_tokens, int32_t* parent,
+                           int32_t* n_nodes, void* stream);
+
 /* The tree mask alone: mask_out[b][i] (uint64, device) has bit j set iff
  * tree node j is node i or one of its ancestors. A sequence whose parent
  * array breaks the rule gets all-zero words and sets HTA_STATUS_BAD_TREE.

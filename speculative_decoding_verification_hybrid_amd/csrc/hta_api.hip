@@ -20,6 +20,7 @@ struct hta_handle_s {
   int* status;       // sticky HTA_STATUS_* bits
   unsigned long long* argmax_part;  // [B*T*kArgmaxMaxSplit] partial argmax keys (hta_accept)
   unsigned* seq_count;              // [B] arrival counters of hta_commit; zero between calls
+  unsigned long long* topk_part;    // [B * kMaxTreeSplit * (kMaxTreeGuesses + 1)] keys (hta_build_tree)
 };
 
 namespace {
@@ -196,6 +197,8 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   off = align256(off + (size_t)max_slots * d.M * sizeof(float));
   const size_t off_ap = off;
   off = align256(off + (size_t)d.B * d.T * hta::kArgmaxMaxSplit * sizeof(unsigned long long));
+  const size_t off_tk = off;
+  off = align256(off + (size_t)d.B * hta::kMaxTreeSplit * (hta::kMaxTreeGuesses + 1) * sizeof(unsigned long long));
   const size_t off_eb = off;
   off = align256(off + (size_t)d.B * sizeof(int));
   const size_t off_ct = off;
@@ -215,6 +218,7 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   h->status = reinterpret_cast<int*>(base + off_st);
   h->argmax_part = reinterpret_cast<unsigned long long*>(base + off_ap);
   h->seq_count = reinterpret_cast<unsigned*>(base + off_ct);
+  h->topk_part = reinterpret_cast<unsigned long long*>(base + off_tk);
   if (hipMemset(base + off_eb, 0, off - off_eb) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws);
@@ -297,6 +301,29 @@ int hta_window_append(hta_handle_t h, const void* k_new, const void* v_new, void
   if (h->dims.T > h->dims.Lcap) return HTA_ERR_UNSUPPORTED;
   return check_hip(hta::launch_window_append(h->dims, k_new, v_new, k_ring, v_ring, pos, h->seq_count, h->status,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int hta_build_tree(hta_handle_t h, const void* logits, int32_t vocab, int32_t logits_dtype, const int32_t* history,
+                   int32_t history_cap, const int32_t* history_len, const hta_tree_params_t* params,
+                   int32_t* tree_tokens, int32_t* parent, int32_t* n_nodes, void* stream) {
+  if (!h || !logits || !history || !history_len || !params || !tree_tokens || !parent || !n_nodes)
+    return HTA_ERR_INVALID_ARG;
+  if (logits_dtype != HTA_F32 && logits_dtype != HTA_BF16) return HTA_ERR_INVALID_ARG;
+  if (params->k < 0 || params->k > HTA_MAX_TREE_GUESSES || params->m < 1 || params->m > HTA_MAX_NGRAM ||
+      params->keep_first < 0 || params->keep_first > 64 || history_cap < 1)
+    return HTA_ERR_INVALID_ARG;
+  for (int r = 0; r < params->k; ++r)
+    if (params->keep[r] < 0 || params->keep[r] > 64) return HTA_ERR_INVALID_ARG;
+  if (vocab < params->k + 1) return HTA_ERR_INVALID_ARG;
+  if (hta::topk_split_for(vocab) > hta::kMaxTreeSplit) return HTA_ERR_UNSUPPORTED;
+  hta::TreeParams p;
+  p.k = params->k;
+  p.m = params->m;
+  p.keep_first = params->keep_first;
+  for (int r = 0; r < hta::kMaxTreeGuesses; ++r) p.keep[r] = r < params->k ? params->keep[r] : 0;
+  return check_hip(hta::launch_build_tree(h->dims, logits, vocab, logits_dtype == HTA_BF16, history, history_cap,
+                                          history_len, p, h->topk_part, tree_tokens, parent, n_nodes, h->status,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int hta_tree_mask(hta_handle_t h, const int32_t* parent, uint64_t* mask_out, void* stream) {

@@ -68,6 +68,19 @@ hipError_t launch_window_attn(const Dims& d, const void* q, const void* k_ring, 
                               int* status, hipStream_t s);
 hipError_t launch_window_append(const Dims& d, const void* k_new, const void* v_new, void* k_ring, void* v_ring,
                                 int* pos, unsigned* count, int* status, hipStream_t s);
+// Draft-tree construction from the last logits (tree_build.hip). part holds
+// B * topk_split_for(V) * (kMaxTreeGuesses + 1) keys.
+constexpr int kMaxTreeGuesses = 31;
+constexpr int kMaxNgram = 8;
+constexpr int kMaxTreeSplit = 64;  // vocabulary up to kMaxTreeSplit * 4096 entries
+struct TreeParams {
+  int k, m, keep_first;
+  int keep[kMaxTreeGuesses];
+};
+int topk_split_for(int V);
+hipError_t launch_build_tree(const Dims& d, const void* logits, int V, bool logits_bf16, const int* history,
+                             int hist_cap, const int* hist_len, const TreeParams& p, unsigned long long* part,
+                             int* tokens, int* parent, int* n_nodes, int* status, hipStream_t s);
 // Occupancy (workgroups per CU) of the chosen prefix kernel, for sizing nwg.
 int prefix_mfma_occupancy(int D, int waves, int qb);
 int prefix_valu_occupancy(int D, bool bf16);

@@ -65,6 +65,26 @@ class HtaConfig(ctypes.Structure):
     ]
 
 
+HTA_MAX_TREE_GUESSES = 31
+HTA_MAX_NGRAM = 8
+
+
+class HtaTreeParams(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_int32),
+        ("m", ctypes.c_int32),
+        ("keep_first", ctypes.c_int32),
+        ("keep", ctypes.c_int32 * HTA_MAX_TREE_GUESSES),
+    ]
+
+
+def make_tree_params(k: int, m: int, keep_first: int, keep) -> HtaTreeParams:
+    p = HtaTreeParams(k=k, m=m, keep_first=keep_first)
+    for r, v in enumerate(keep):
+        p.keep[r] = int(v)
+    return p
+
+
 class HtaPlan(ctypes.Structure):
     _fields_ = [
         ("path", ctypes.c_int32),
@@ -94,6 +114,8 @@ _SIGNATURES = {
     "hta_prefix_attn": (ctypes.c_int, [_vp] * 7 + [_vp]),
     "hta_cross_attn": (ctypes.c_int, [_vp] * 7 + [_vp]),
     "hta_window_attn": (ctypes.c_int, [_vp] * 9 + [_vp]),
+    "hta_build_tree": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _vp, ctypes.POINTER(HtaTreeParams)]
+                       + [_vp] * 3 + [_vp]),
     "hta_window_append": (ctypes.c_int, [_vp] * 6 + [_vp]),
     "hta_prefix_partials": (ctypes.c_int, [_vp] * 5 + [_vp]),
     "hta_merge_prefix": (ctypes.c_int, [_vp] * 4 + [_vp]),
@@ -284,6 +306,33 @@ def hta_cross_attn(h: Handle, q, k_cache, v_cache, prefix_len, out, lse, stream=
     ]
     _check(load_library().hta_cross_attn(_vp(h.ptr), *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
            "hta_cross_attn")
+
+
+def hta_build_tree(h: Handle, logits, history, history_len, params: HtaTreeParams, tree_tokens, parent, n_nodes,
+                   stream=None) -> None:
+    """logits [B, V] float32 or bfloat16 (last position); history [B, cap] int32; see include/hta.h."""
+    import torch
+    B, _, _, _, T, _ = h.dims
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits must be a [B, V] tensor")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"logits has dtype {logits.dtype}, expected float32 or bfloat16")
+    V = int(logits.shape[1])
+    cap = int(history.shape[1]) if isinstance(history, torch.Tensor) and history.dim() == 2 else -1
+    ldt = HTA_BF16 if logits.dtype == torch.bfloat16 else HTA_F32
+    lp = _tensor(logits, "logits", logits.dtype, (B, V))
+    hp = _tensor(history, "history", torch.int32, (B, cap))
+    args = [
+        _tensor(history_len, "history_len", torch.int32, (B,)),
+    ]
+    outs = [
+        _tensor(tree_tokens, "tree_tokens", torch.int32, (B, T)),
+        _tensor(parent, "parent", torch.int32, (B, T)),
+        _tensor(n_nodes, "n_nodes", torch.int32, (B,)),
+    ]
+    _check(load_library().hta_build_tree(_vp(h.ptr), _vp(lp), V, ldt, _vp(hp), cap, _vp(args[0]),
+                                         ctypes.byref(params), *[_vp(a) for a in outs], _vp(_stream_ptr(stream))),
+           "hta_build_tree")
 
 
 def hta_window_attn(h: Handle, q, k_ring, v_ring, k_new, v_new, pos, out, lse, stream=None) -> None:

@@ -110,6 +110,8 @@ def test_null_arguments_fail_before_any_hip_call(lib):
     assert lib.hta_cross_attn(None, *([None] * 7)) == hta.HTA_ERR_INVALID_ARG
     assert lib.hta_window_attn(None, *([None] * 9)) == hta.HTA_ERR_INVALID_ARG
     assert lib.hta_window_append(None, *([None] * 6)) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_build_tree(None, None, 100, hta.HTA_BF16, None, 10, None, None, None, None, None,
+                              None) == hta.HTA_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

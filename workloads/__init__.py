@@ -21,3 +21,4 @@ from .gen import (  # noqa: F401
 )
 from .accept_gen import AcceptCase, make_accept_case  # noqa: F401,E402
 from .draft_gen import WindowCase, make_window_case  # noqa: F401,E402
+from .tree_gen import TreeCase, make_tree_case  # noqa: F401,E402
