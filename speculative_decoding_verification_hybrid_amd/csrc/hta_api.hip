@@ -21,6 +21,7 @@ struct hta_handle_s {
   unsigned long long* argmax_part;  // [B*T*kArgmaxMaxSplit] partial argmax keys (hta_accept)
   unsigned* seq_count;              // [B] arrival counters of hta_commit; zero between calls
   unsigned long long* topk_part;    // [B * kMaxTreeSplit * (kMaxTreeGuesses + 1)] keys (hta_build_tree)
+  int* tree_aux;                    // [2 * B * (kMaxTreeGuesses + 1)] match ends, x1 + guesses
 };
 
 namespace {
@@ -199,6 +200,8 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   off = align256(off + (size_t)d.B * d.T * hta::kArgmaxMaxSplit * sizeof(unsigned long long));
   const size_t off_tk = off;
   off = align256(off + (size_t)d.B * hta::kMaxTreeSplit * (hta::kMaxTreeGuesses + 1) * sizeof(unsigned long long));
+  const size_t off_ta = off;
+  off = align256(off + 2 * (size_t)d.B * (hta::kMaxTreeGuesses + 1) * sizeof(int));
   const size_t off_eb = off;
   off = align256(off + (size_t)d.B * sizeof(int));
   const size_t off_ct = off;
@@ -219,6 +222,7 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   h->argmax_part = reinterpret_cast<unsigned long long*>(base + off_ap);
   h->seq_count = reinterpret_cast<unsigned*>(base + off_ct);
   h->topk_part = reinterpret_cast<unsigned long long*>(base + off_tk);
+  h->tree_aux = reinterpret_cast<int*>(base + off_ta);
   if (hipMemset(base + off_eb, 0, off - off_eb) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws);
@@ -322,7 +326,7 @@ int hta_build_tree(hta_handle_t h, const void* logits, int32_t vocab, int32_t lo
   p.keep_first = params->keep_first;
   for (int r = 0; r < hta::kMaxTreeGuesses; ++r) p.keep[r] = r < params->k ? params->keep[r] : 0;
   return check_hip(hta::launch_build_tree(h->dims, logits, vocab, logits_dtype == HTA_BF16, history, history_cap,
-                                          history_len, p, h->topk_part, tree_tokens, parent, n_nodes, h->status,
+                                          history_len, p, h->topk_part, h->tree_aux, tree_tokens, parent, n_nodes, h->status,
                                           static_cast<hipStream_t>(stream)));
 }
 

@@ -78,9 +78,10 @@ struct TreeParams {
   int keep[kMaxTreeGuesses];
 };
 int topk_split_for(int V);
+// aux: 2 * B * (kMaxTreeGuesses + 1) ints (match ends, x1 + guesses).
 hipError_t launch_build_tree(const Dims& d, const void* logits, int V, bool logits_bf16, const int* history,
                              int hist_cap, const int* hist_len, const TreeParams& p, unsigned long long* part,
-                             int* tokens, int* parent, int* n_nodes, int* status, hipStream_t s);
+                             int* aux, int* tokens, int* parent, int* n_nodes, int* status, hipStream_t s);
 // Occupancy (workgroups per CU) of the chosen prefix kernel, for sizing nwg.
 int prefix_mfma_occupancy(int D, int waves, int qb);
 int prefix_valu_occupancy(int D, bool bf16);

@@ -16,15 +16,18 @@
 // Kernels:
 //  * topk_partial_kernel: B*split workgroups; each reduces its slice of a
 //    logit row to its kk = k+1 largest 64-bit keys (order-preserving value
-//    bits above, V-1-index below), by kk rounds of "largest key below the last
-//    one" over keys held in registers.
-//  * tree_build_kernel: one workgroup per sequence merges the split lists the
-//    same way, then streams the sequence (history then x1) through LDS in
-//    chunks. Every query-2 gram shares its first m-1 tokens (the m-1 tokens
-//    ending with x1), so a position needs one compare of that tail plus a
-//    lookup of its token among the guesses, and one compare for query 1;
-//    the latest match per query is kept with an LDS atomic max. Thread 0
-//    then lays out the tree (at most 64 nodes).
+//    bits above, V-1-index below) by kk rounds of "largest key below the last
+//    one", run per wave with DPP reductions (no barriers), then over the four
+//    waves' lists. It also resets the sequence's match slots.
+//  * tree_scan_kernel: (B, sequence/kScanChunk) workgroups; each merges the
+//    split lists the same way (x1 and the guesses), stages its chunk of the
+//    sequence (history then x1) in LDS and tests every gram ending in it.
+//    Every query-2 gram shares its first m-1 tokens (the m-1 tokens ending
+//    with x1), so a position needs one compare of that tail plus a lookup of
+//    its token among the guesses, and one compare for query 1; the latest
+//    match per query is kept with a device-wide atomic max.
+//  * tree_layout_kernel: one workgroup per sequence sizes the branches, then
+//    writes one node per thread.
 #include "common.h"
 #include "hta_internal.h"
 
@@ -34,7 +37,7 @@ namespace {
 constexpr int kTopThreads = 256;
 constexpr int kTopEPT = 16;                          // keys per thread in a slice
 constexpr int kTopChunk = kTopThreads * kTopEPT;     // vocabulary entries per workgroup
-constexpr int kHistChunk = 8192;                     // sequence tokens per LDS pass
+constexpr int kScanChunk = 2048;                     // gram end positions per scan workgroup
 
 __device__ __forceinline__ unsigned ordered_bits(float x) {
   const unsigned u = __float_as_uint(x);
@@ -49,56 +52,59 @@ __device__ __forceinline__ unsigned key_index(unsigned long long k) {
 __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long x) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)x, CTRL, 0xf, 0xf, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(x >> 32), CTRL, 0xf, 0xf, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+// Largest key of the wave, in every lane: DPP within rows of 16 (partners at
+// lane distance 1, 2, and rotations by 4 and 8), then the row swaps.
 __device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const unsigned lo = __shfl_xor((unsigned)k, off), hi = __shfl_xor((unsigned)(k >> 32), off);
-    k = umax64(k, ((unsigned long long)hi << 32) | lo);
-  }
-  return k;
+  k = umax64(k, dpp64<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = umax64(k, dpp64<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = umax64(k, dpp64<0x124>(k));  // row_ror:4
+  k = umax64(k, dpp64<0x128>(k));  // row_ror:8
+  auto lo = __builtin_amdgcn_permlane16_swap((unsigned)k, (unsigned)k, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(k >> 32), (unsigned)(k >> 32), false, false);
+  k = umax64(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
+  lo = __builtin_amdgcn_permlane32_swap((unsigned)k, (unsigned)k, false, false);
+  hi = __builtin_amdgcn_permlane32_swap((unsigned)(k >> 32), (unsigned)(k >> 32), false, false);
+  return umax64(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
 }
 
-// kk rounds over the kTopEPT keys each thread holds (0 = no key): out[j] =
-// j-th largest key of the workgroup (0 past the end). red: kTopThreads/64 slots.
-__device__ void select_top(const unsigned long long* mine, int kk, unsigned long long* out,
-                           unsigned long long* red, unsigned long long* bcast) {
+// kk rounds over the E keys each lane of one wave holds (0 = no key): lane 0
+// writes out[j] = the j-th largest key of the wave (0 past the end). No
+// barriers: every lane learns each round's maximum from wave_max64.
+template <int E>
+__device__ void select_top_wave(const unsigned long long* mine, int kk, unsigned long long* out) {
   unsigned long long bound = ~0ull;  // every key is below it
   for (int j = 0; j < kk; ++j) {
     unsigned long long best = 0ull;
 #pragma unroll
-    for (int e = 0; e < kTopEPT; ++e)
+    for (int e = 0; e < E; ++e)
       if (mine[e] < bound) best = umax64(best, mine[e]);
     best = wave_max64(best);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned long long k = red[0];
-#pragma unroll
-      for (int w = 1; w < kTopThreads / 64; ++w) k = umax64(k, red[w]);
-      out[j] = k;
-      *bcast = k;
-    }
-    __syncthreads();
-    bound = *bcast;
-    if (bound == 0ull) {  // fewer keys than kk: the rest stay 0
-      for (int i = j + 1 + (int)threadIdx.x; i < kk; i += kTopThreads) out[i] = 0ull;
-      break;
-    }
+    if ((threadIdx.x & 63) == 0) out[j] = best;
+    bound = best;  // 0 once the keys run out: later rounds write 0 too
   }
 }
 
+// grid: B*split workgroups. Each wave selects the kk largest of its 1024 keys,
+// then wave 0 selects the kk largest of the four lists. Workgroup 0 of a
+// sequence also resets that sequence's match slots for the scan.
 template <bool BF16>
 __global__ void __launch_bounds__(kTopThreads) topk_partial_kernel(const void* logits, int V, int split, int kk,
-                                                                   unsigned long long* part) {
-  __shared__ unsigned long long red[kTopThreads / 64];
-  __shared__ unsigned long long bcast;
-  __shared__ unsigned long long out[kMaxTreeGuesses + 1];
+                                                                   unsigned long long* part, int* best_g) {
+  __shared__ unsigned long long wave_top[kTopThreads / 64][kMaxTreeGuesses + 1];
   const int b = blockIdx.x / split, s = blockIdx.x % split;
   const int lo = s * kTopChunk;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (s == 0 && threadIdx.x < kMaxTreeGuesses + 1) best_g[b * (kMaxTreeGuesses + 1) + threadIdx.x] = -1;
   unsigned long long mine[kTopEPT];
 #pragma unroll
   for (int e = 0; e < kTopEPT; ++e) {
-    const int i = lo + (int)threadIdx.x + e * kTopThreads;
+    const int i = lo + wv * (64 * kTopEPT) + lane + e * 64;
     float x = 0.f;
     if (i < V) {
       if (BF16) x = bf16_bits_to_float(static_cast<const unsigned short*>(logits)[(size_t)b * V + i]);
@@ -106,9 +112,17 @@ __global__ void __launch_bounds__(kTopThreads) topk_partial_kernel(const void* l
     }
     mine[e] = i < V ? make_key(x, (unsigned)i) : 0ull;
   }
-  select_top(mine, kk, out, red, &bcast);
+  select_top_wave<kTopEPT>(mine, kk, wave_top[wv]);
   __syncthreads();
-  for (int j = threadIdx.x; j < kk; j += kTopThreads) part[((size_t)b * split + s) * (kMaxTreeGuesses + 1) + j] = out[j];
+  if (wv == 0) {
+    unsigned long long m2[(kTopThreads / 64) * (kMaxTreeGuesses + 1) / 64];
+#pragma unroll
+    for (int e = 0; e < (int)(sizeof(m2) / sizeof(m2[0])); ++e) {
+      const int i = lane + 64 * e;  // entry i of the (kTopThreads/64) lists of kk
+      m2[e] = i < (kTopThreads / 64) * kk ? wave_top[i / kk][i % kk] : 0ull;
+    }
+    select_top_wave<(int)(sizeof(m2) / sizeof(m2[0]))>(m2, kk, part + ((size_t)b * split + s) * (kMaxTreeGuesses + 1));
+  }
 }
 
 struct TreeArgs {
@@ -119,28 +133,114 @@ struct TreeArgs {
   const int* hist_len;
   TreeParams p;
   int T;
+  int* best_g;  // [B][kMaxTreeGuesses+1] latest match end per query ([0] query 1, [1+r] guess r)
+  int* top_g;   // [B][kMaxTreeGuesses+1] x1 then the guesses
   int* tokens;
   int* parent;
   int* n_nodes;
   int* status;
 };
 
-__global__ void __launch_bounds__(kTopThreads) tree_build_kernel(TreeArgs a) {
-  __shared__ unsigned long long red[kTopThreads / 64];
-  __shared__ unsigned long long bcast;
+// The split lists of sequence b merged by wave 0 into top[0 .. kk).
+__device__ void merge_top(const TreeArgs& a, int b, unsigned long long* top) {
+  if ((threadIdx.x >> 6) != 0) return;
+  constexpr int E = kMaxTreeSplit * (kMaxTreeGuesses + 1) / 64;
+  unsigned long long mine[E];
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;  // entry i of split*kk
+    mine[e] = i < a.split * a.kk ? a.part[((size_t)b * a.split + i / a.kk) * (kMaxTreeGuesses + 1) + i % a.kk]
+                                 : 0ull;
+  }
+  select_top_wave<E>(mine, a.kk, top);
+}
+
+// grid: (B, scan workgroups): workgroup c looks for the queries among the grams
+// ending at positions [c*kScanChunk, (c+1)*kScanChunk) of the sequence.
+__global__ void __launch_bounds__(kTopThreads) tree_scan_kernel(TreeArgs a) {
   __shared__ unsigned long long top[kMaxTreeGuesses + 1];
-  __shared__ int seqs[kHistChunk + kMaxNgram];
-  __shared__ int q1s[kMaxNgram];   // query 1
-  __shared__ int tail[kMaxNgram];  // the m-1 tokens ending with x1 (query 2 without its guess)
-  __shared__ int best[kMaxTreeGuesses + 1];  // latest match end: [0] query 1, [1 + r] guess r
+  __shared__ int seqs[kScanChunk + kMaxNgram];
+  const int b = blockIdx.x, c = blockIdx.y;
+  const int tid = (int)threadIdx.x;
+  const int k = a.p.k, m = a.p.m;
+  const int L = a.hist_len[b];
+  if (L < 0 || L > a.hist_cap) return;  // the layout kernel reports it
+  const int n = L + 1;                   // history, then x1
+  const int c0 = c * kScanChunk;
+  if (c0 >= n) return;
+  const int* hist = a.history + (size_t)b * a.hist_cap;
+  // this chunk's tokens (and the m-1 before it) are requested before the merge
+  const int lo = c0 - (m - 1);
+  const int cnt = min(kScanChunk, n - c0) + (m - 1);
+  constexpr int kIters = (kScanChunk + kMaxNgram + kTopThreads - 1) / kTopThreads;
+  int v[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int i = tid + it * kTopThreads, j = lo + i;
+    v[it] = (i < cnt && j >= 0 && j < L) ? hist[j] : -1;
+  }
+  merge_top(a, b, top);
+  __syncthreads();
+  const int x1 = (int)key_index(top[0]);
+  if (c == 0 && tid <= k) a.top_g[b * (kMaxTreeGuesses + 1) + tid] = (int)key_index(top[tid]);
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int i = tid + it * kTopThreads;
+    if (i < cnt) seqs[i] = lo + i == L ? x1 : v[it];
+  }
+  // query 1 = seq[n-m .. n-1]; query 2 = seq[n-m+1 .. n-1] + guess
+  int q1r[kMaxNgram], tailr[kMaxNgram];
+#pragma unroll
+  for (int t = 0; t < kMaxNgram; ++t) {
+    const int j1 = n - m + t, j2 = n - (m - 1) + t;
+    q1r[t] = (t < m && j1 >= 0) ? (j1 < L ? hist[j1] : x1) : -1;
+    tailr[t] = (t < m - 1 && j2 >= 0) ? (j2 < L ? hist[j2] : x1) : -1;
+  }
+  __syncthreads();
+  const bool q1_possible = m <= n;
+  const bool q2_possible = m - 1 <= n && k > 0;
+  const int npos = min(kScanChunk, n - c0);
+  int* bg = a.best_g + b * (kMaxTreeGuesses + 1);
+#pragma unroll 4
+  for (int it = 0; it < kScanChunk / kTopThreads; ++it) {
+    const int i = tid + it * kTopThreads;
+    const int p = c0 + i;  // end position of the gram; w[t] = seq[p-m+1+t]
+    int w[kMaxNgram];
+#pragma unroll
+    for (int t = 0; t < kMaxNgram; ++t) w[t] = t < m ? seqs[i + t] : 0;
+    const bool here = i < npos && p >= m - 1;
+    bool e1 = here && q1_possible && p < n - 1;  // query 1 may not match itself
+    bool e2 = here && q2_possible;
+#pragma unroll
+    for (int t = 0; t < kMaxNgram; ++t) {
+      if (t < m) e1 &= w[t] == q1r[t];
+      if (t < m - 1) e2 &= w[t] == tailr[t];
+    }
+    if (e1) atomicMax(&bg[0], p);
+    if (e2) {
+      int tk = w[0];
+#pragma unroll
+      for (int t = 1; t < kMaxNgram; ++t)
+        if (t == m - 1) tk = w[t];
+      for (int r = 0; r < k; ++r)
+        if (tk == (int)key_index(top[1 + r])) atomicMax(&bg[1 + r], p);
+    }
+  }
+}
+
+// grid: B workgroups: sizes the branches, then writes one node per thread.
+__global__ void __launch_bounds__(kTopThreads) tree_layout_kernel(TreeArgs a) {
+  __shared__ int br_first[kMaxTreeGuesses + 2];
+  __shared__ int best[kMaxTreeGuesses + 1];
+  __shared__ int topt[kMaxTreeGuesses + 1];
+  __shared__ int n_used;
   const int b = blockIdx.x;
   const int tid = (int)threadIdx.x;
-  const int T = a.T, k = a.p.k, m = a.p.m;
+  const int T = a.T, k = a.p.k;
   const int L = a.hist_len[b];
-  const int* hist = a.history + (size_t)b * a.hist_cap;
   int* tok_out = a.tokens + (size_t)b * T;
   int* par_out = a.parent + (size_t)b * T;
-
   if (L < 0 || L > a.hist_cap) {
     for (int i = tid; i < T; i += kTopThreads) {
       tok_out[i] = -1;
@@ -152,92 +252,51 @@ __global__ void __launch_bounds__(kTopThreads) tree_build_kernel(TreeArgs a) {
     }
     return;
   }
-
-  // 1. merge the split lists: x1 and the ranked guesses
-  unsigned long long mine[kTopEPT];
-#pragma unroll
-  for (int e = 0; e < kTopEPT; ++e) {
-    const int i = tid + e * kTopThreads;  // entry i of split*kk
-    mine[e] = i < a.split * a.kk
-                  ? a.part[((size_t)b * a.split + i / a.kk) * (kMaxTreeGuesses + 1) + i % a.kk]
-                  : 0ull;
-  }
-  select_top(mine, a.kk, top, red, &bcast);
-  __syncthreads();
-  const int x1 = (int)key_index(top[0]);
-  // the sequence: hist[0 .. L-1], then x1 at position L; n = L + 1 tokens
   const int n = L + 1;
+  const int* hist = a.history + (size_t)b * a.hist_cap;
+  if (tid <= k) {
+    best[tid] = a.best_g[b * (kMaxTreeGuesses + 1) + tid];
+    topt[tid] = a.top_g[b * (kMaxTreeGuesses + 1) + tid];
+  }
+  __syncthreads();
+  const int x1 = topt[0];
   auto seq_at = [&](int j) { return j < L ? hist[j] : x1; };
-  if (tid < m) {
-    q1s[tid] = n - m + tid >= 0 ? seq_at(n - m + tid) : -1;
-    if (tid < m - 1) tail[tid] = n - (m - 1) + tid >= 0 ? seq_at(n - (m - 1) + tid) : -1;
-  }
-  if (tid <= k) best[tid] = -1;
-  __syncthreads();
-
-  // 2. one pass over the sequence, kHistChunk positions at a time (with the m-1
-  // tokens before each chunk)
-  const bool q1_possible = m <= n;
-  const bool q2_possible = m - 1 <= n;
-  for (int c0 = 0; c0 < n; c0 += kHistChunk) {
-    const int lo = c0 - (m - 1);
-    const int cnt = min(kHistChunk, n - c0) + (m - 1);
-    for (int i = tid; i < cnt; i += kTopThreads) {
-      const int j = lo + i;
-      seqs[i] = j >= 0 ? seq_at(j) : -1;
-    }
-    __syncthreads();
-    for (int i = tid; i < min(kHistChunk, n - c0); i += kTopThreads) {
-      const int p = c0 + i;        // end position of the gram
-      if (p < m - 1) continue;     // a gram needs m tokens
-      const int* w = &seqs[i];     // w[0 .. m-1] = seq[p-m+1 .. p]
-      if (q1_possible && p < n - 1) {  // query 1 may not match itself
-        bool eq = true;
-        for (int t = 0; t < m; ++t) eq &= w[t] == q1s[t];
-        if (eq) atomicMax(&best[0], p);
-      }
-      if (q2_possible && k > 0) {
-        bool eq = true;
-        for (int t = 0; t < m - 1; ++t) eq &= w[t] == tail[t];
-        if (eq) {
-          const int tk = w[m - 1];
-          for (int r = 0; r < k; ++r)
-            if (tk == (int)key_index(top[1 + r])) atomicMax(&best[1 + r], p);
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // 3. lay out the tree
-  for (int i = tid; i < T; i += kTopThreads) {
-    tok_out[i] = -1;
-    par_out[i] = 0;
-  }
-  __syncthreads();
   if (tid == 0) {
-    int used = 0;
-    auto add = [&](int tokv, int par) {
-      if (used >= T) return -1;
-      tok_out[used] = tokv;
-      par_out[used] = par;
-      return used++;
-    };
-    add(x1, -1);
-    if (best[0] >= 0) {
-      int par = 0;
-      for (int t = 0; t < a.p.keep_first && best[0] + 1 + t < n && par >= 0; ++t)
-        par = add(seq_at(best[0] + 1 + t), par);
-    }
+    int used = 1;  // node 0 = x1
+    const int c1 = best[0] >= 0 ? min(a.p.keep_first, n - 1 - best[0]) : 0;
+    br_first[0] = used;
+    used += c1;
     for (int r = 0; r < k; ++r) {
-      const int node = add((int)key_index(top[1 + r]), 0);
-      if (node < 0) break;
-      const int pe = best[1 + r];
-      if (pe < 0) continue;
-      int par = node;
-      for (int t = 0; t < a.p.keep[r] && pe + 1 + t < n && par >= 0; ++t) par = add(seq_at(pe + 1 + t), par);
+      br_first[1 + r] = used;
+      used += 1 + (best[1 + r] >= 0 ? min(a.p.keep[r], n - 1 - best[1 + r]) : 0);
     }
-    a.n_nodes[b] = used;
+    br_first[k + 1] = used;
+    n_used = min(used, T);
+    a.n_nodes[b] = n_used;
+  }
+  __syncthreads();
+  for (int i = tid; i < T; i += kTopThreads) {
+    int tv = -1, pv = 0;
+    if (i == 0) {
+      tv = x1;
+      pv = -1;
+    } else if (i < n_used) {
+      int br = 0;
+      while (i >= br_first[br + 1]) ++br;  // br_first is non-decreasing; i < br_first[k + 1]
+      const int o = i - br_first[br];
+      if (br == 0) {
+        tv = seq_at(best[0] + 1 + o);
+        pv = o == 0 ? 0 : i - 1;
+      } else if (o == 0) {
+        tv = topt[br];
+        pv = 0;
+      } else {
+        tv = seq_at(best[br] + o);
+        pv = i - 1;
+      }
+    }
+    tok_out[i] = tv;
+    par_out[i] = pv;
   }
 }
 
@@ -247,15 +306,17 @@ int topk_split_for(int V) { return (V + kTopChunk - 1) / kTopChunk; }
 
 hipError_t launch_build_tree(const Dims& d, const void* logits, int V, bool logits_bf16, const int* history,
                              int hist_cap, const int* hist_len, const TreeParams& p, unsigned long long* part,
-                             int* tokens, int* parent, int* n_nodes, int* status, hipStream_t s) {
+                             int* aux, int* tokens, int* parent, int* n_nodes, int* status, hipStream_t s) {
   const int split = topk_split_for(V);
   const int kk = p.k + 1;
+  int* best_g = aux;
+  int* top_g = aux + (size_t)d.B * (kMaxTreeGuesses + 1);
   if (logits_bf16)
     hipLaunchKernelGGL(topk_partial_kernel<true>, dim3(d.B * split), dim3(kTopThreads), 0, s, logits, V, split, kk,
-                       part);
+                       part, best_g);
   else
     hipLaunchKernelGGL(topk_partial_kernel<false>, dim3(d.B * split), dim3(kTopThreads), 0, s, logits, V, split,
-                       kk, part);
+                       kk, part, best_g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TreeArgs a;
@@ -267,11 +328,18 @@ hipError_t launch_build_tree(const Dims& d, const void* logits, int V, bool logi
   a.hist_len = hist_len;
   a.p = p;
   a.T = d.T;
+  a.best_g = best_g;
+  a.top_g = top_g;
   a.tokens = tokens;
   a.parent = parent;
   a.n_nodes = n_nodes;
   a.status = status;
-  hipLaunchKernelGGL(tree_build_kernel, dim3(d.B), dim3(kTopThreads), 0, s, a);
+  // positions 0 .. hist_cap (the longest sequence is the full history plus x1)
+  const int chunks = (hist_cap + 1 + kScanChunk - 1) / kScanChunk;
+  hipLaunchKernelGGL(tree_scan_kernel, dim3(d.B, chunks), dim3(kTopThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree_layout_kernel, dim3(d.B), dim3(kTopThreads), 0, s, a);
   return hipGetLastError();
 }
 
