@@ -24,7 +24,10 @@ the oracle's accept + commit on the same inputs beside it. A third leg
 ("draft_cross_attn") times the drafter's cross-attention over the same 32k
 cache with one draft token (hta_cross_attn, the small-row DOT kernel), and a
 fourth ("tree_build") the construction of the next draft tree from the last
-logits and a 32k-token history (hta_build_tree).
+logits and a 32k-token history (hta_build_tree). "configs" reports the layer
+at all five configurations (p10/p50/p90 over graph replays, each against the
+HBM peak and against a measured device copy, with one oracle run each), and
+"copy_bw_gbs" that copy's bandwidth.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --copy-calibration   (adds 8 launches of a plain elementwise
@@ -70,6 +73,7 @@ def parse():
     ap.add_argument("--no-accept", action="store_true", help="skip the accept + commit leg")
     ap.add_argument("--no-draft", action="store_true", help="skip the draft cross-attention leg")
     ap.add_argument("--no-tree", action="store_true", help="skip the tree-construction leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the five-configuration sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run 8 copy-like 256 MiB elementwise kernels before timing")
     return ap.parse_args()
@@ -401,6 +405,97 @@ def tree_build_row(w, steps, warmup, cpu_seconds):
     return row
 
 
+def copy_bandwidth():
+    """Device-to-device copy of 512 MiB (read + write bytes / time): the measured
+    bandwidth the layer figures are also compared with."""
+    import torch
+    n = 256 << 20  # int16 elements = 512 MiB
+    src = torch.ones(n, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 2 / (ms * 1e-3) / 1e9
+
+
+def all_configs_row(copy_gbs, cpu):
+    """hta_verify_attn at each of the five layer configurations: KV rotated over
+    >= 512 MB of replicas, 10 graph replays of 20 calls each; p10/p50/p90 of the
+    per-call time over the replays. With cpu, one oracle run per configuration."""
+    import torch
+    from speculative_decoding_verification_hybrid_amd import hta
+    from workloads import CONFIGS, make_workload
+
+    rows = {}
+    for key in sorted(CONFIGS):
+        w = make_workload(key)
+        kv_bytes, total_bytes = algorithmic_bytes(w)
+        if w.dtype == "bf16":
+            dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+            odt = torch.bfloat16
+        else:
+            dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+            odt = torch.float32
+        R = max(1, int(np.ceil(512e6 / kv_bytes)))
+        kc0, vc0 = dev(w.k_cache), dev(w.v_cache)
+        kcs = [kc0] + [kc0.clone() for _ in range(R - 1)]
+        vcs = [vc0] + [vc0.clone() for _ in range(R - 1)]
+        q, kt, vt = dev(w.q), dev(w.k_tree), dev(w.v_tree)
+        parent, plen = torch.from_numpy(w.parent).cuda(), torch.from_numpy(w.prefix_len).cuda()
+        out = torch.empty(w.B, w.Hq, w.T, w.D, dtype=odt, device="cuda")
+        lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device="cuda")
+        h = hta.hta_create(hta.make_config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D,
+                                           tree_nodes=w.T, kv_capacity=w.Lcap, dtype=w.dtype,
+                                           softmax_scale=w.scale))
+        path = hta.hta_get_plan(h)["path"]
+        n_call = 20
+        for i in range(5):
+            hta.hta_verify_attn(h, q, kcs[i % R], vcs[i % R], kt, vt, parent, plen, out, lse)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_call):
+                hta.hta_verify_attn(h, q, kcs[i % R], vcs[i % R], kt, vt, parent, plen, out, lse,
+                                    torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n_call * 1e3)
+        status = hta.hta_get_status(h)
+        hta.hta_destroy(h)
+        del g, kcs, vcs
+        torch.cuda.empty_cache()
+        p10, p50, p90 = (float(np.percentile(per, x)) for x in (10, 50, 90))
+        gbs = total_bytes / (p50 * 1e-6) / 1e9
+        row = {"workload": CONFIGS[key].name, "path": path, "kv_replicas": R,
+               "layer_us_p10_p50_p90": [round(p10, 3), round(p50, 3), round(p90, 3)],
+               "gbs": round(gbs, 1), "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+               "pct_copy_bw": round(100 * gbs / copy_gbs, 2),
+               "tokens_per_s_verified": round(w.B * w.T / (p50 * 1e-6), 1), "status_ok": status == 0}
+        if cpu:
+            import oracle
+            t0 = time.perf_counter()
+            oracle.verify_attn(w)
+            row["oracle_s"] = round(time.perf_counter() - t0, 3)
+        rows[str(key)] = row
+    return rows
+
+
 def accept_cpu_baseline(case, w, min_seconds, accept_bytes):
     """The oracle's accept + commit on the same logits and tree; the commit writes into a
     cache of room T behind a T-row prefix (its cost does not depend on the prefix)."""
@@ -560,6 +655,11 @@ def main():
     if not args.no_draft:
         res["draft_cross_attn"] = draft_cross_row(w, args.steps, args.warmup, args.replica_bytes,
                                                   0 if args.no_cpu_baseline else args.cpu_seconds / 4)
+    if not args.no_configs:
+        cgbs = copy_bandwidth()
+        res["copy_bw_gbs"] = round(cgbs, 1)
+        res["pct_copy_bw"] = round(100 * value / cgbs, 2)
+        res["configs"] = all_configs_row(cgbs, not args.no_cpu_baseline)
     if not args.no_tree:
         res["tree_build"] = tree_build_row(w, args.steps, args.warmup,
                                            0 if args.no_cpu_baseline else args.cpu_seconds / 4)
