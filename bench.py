@@ -58,6 +58,8 @@ ACCEPT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "argmax_accept_llama8b_voca
 ACCEPT_SRC = os.path.join(CSRC, "accept.hip")
 DOT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_dot_llama8b_draft_32k_traffic.txt")
 DOT_SRC = os.path.join(CSRC, "prefix_dot.hip")
+MFMA_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefix_mfma_llama8b_32k_mfma_lds_counters.txt")
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def parse():
@@ -616,6 +618,9 @@ def main():
     value = total_bytes / (ms * 1e-3) / 1e9
     prefix_gbs = kv_bytes / (pms * 1e-3) / 1e9
     traffic = traffic_from_profile()
+    # bf16 MFMA work of one prefix launch: QK^T and PV, 2 flops per multiply-add each
+    mfma_flops = 4 * w.Hq * w.T * w.D * int(w.prefix_len.sum())
+    mfma_tflops = mfma_flops / (pms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -648,6 +653,16 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(pms * 1e3, 3),
             "algorithmic_bytes_per_launch": kv_bytes,
+            # the same launches against the bf16 matrix-core peak; busy fractions from a
+            # committed rocprofv3 counter pass on the current kernel source (else null)
+            "mfma": {
+                "flops_per_launch": mfma_flops,
+                "achieved_tflops": round(mfma_tflops, 1),
+                "peak_tflops": PEAK_BF16_MFMA_TFLOPS,
+                "frac": round(mfma_tflops / PEAK_BF16_MFMA_TFLOPS, 4),
+                "busy_counters": traffic_from_profile(MFMA_COUNTERS_FILE, PREFIX_SRC, "mfma_busy"),
+                "lds_util_counters": traffic_from_profile(MFMA_COUNTERS_FILE, PREFIX_SRC, "lds_util"),
+            },
         },
     }
     if not args.no_cpu_baseline:
