@@ -83,14 +83,30 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   size_t o_stride, l_stride;
   float l_scale;
   if (SLOTS) {
-    const int Lraw = a.prefix_len[b];
+    // One pass over the batch's prefix lengths gives the total tile count and
+    // segment (b, g)'s first tile and count (the values total_tiles and
+    // segment_tiles compute); err_b is requested beside it, so the row pays one
+    // round trip here rather than one per quantity.
+    // (a pointer select, not a branch, so the load is not waited on before the loop below)
+    const int err_raw = *(a.err_b != nullptr ? a.err_b + b : a.prefix_len + b);
+    unsigned seq_tiles = 0, before = 0;
+    int count = 0, Lraw = 0;
+#pragma unroll 4
+    for (int bb = 0; bb < a.B; ++bb) {
+      const int Lb = a.prefix_len[bb];
+      const int nt = tiles_of((Lb < 0 || Lb > a.Lcap) ? 0 : Lb, NK) + a.tree_tiles;
+      seq_tiles += (unsigned)nt;
+      if (bb < b) before += (unsigned)nt;
+      if (bb == b) {
+        count = nt;
+        Lraw = Lb;
+      }
+    }
     const bool bad_prefix = Lraw < 0 || Lraw > a.Lcap;
-    bad = bad_prefix || (a.err_b != nullptr && a.err_b[b] != 0);
+    bad = bad_prefix || (a.err_b != nullptr && err_raw != 0);
     if (bad_prefix && h == 0 && node == 0 && lane == 0) atomicOr(a.status, kStatusBadPrefix);
-    TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles);
-    unsigned first;
-    int count;
-    segment_tiles(a.prefix_len, a.Hkv, a.Lcap, NK, a.tree_tiles, b, g, &first, &count);
+    TT = seq_tiles * (unsigned)a.Hkv;
+    const unsigned first = before * (unsigned)a.Hkv + (unsigned)(g * count);
     int p_first = 0;
     if (count > 0) {
       w_first = split_owner(first, a.nwg, TT);
@@ -120,36 +136,44 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int k0 = pg; k0 < p_count; k0 += PG * UNROLL) {
     float lk[UNROLL], ov[UNROLL][8];
+    // Which of this step's parts hold nothing (past the end, or a workgroup
+    // that owns no tile) is known before any load, so every load of the step
+    // is issued before the first wait.
+    bool dead[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      dead[u] = k0 + u * PG >= p_count;
+      if (SLOTS && maybe_empty) {
+        const unsigned wk = w_first + (unsigned)min(k0 + u * PG, p_count - 1);
+        dead[u] = dead[u] || split_begin(wk, a.nwg, TT) == split_begin(wk + 1, a.nwg, TT);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int k = min(k0 + u * PG, p_count - 1);  // in-bounds; ignored past the end
-      float l = l_base[(size_t)k * l_stride] * l_scale;
-      if (k0 + u * PG >= p_count) l = -__builtin_inff();
-      if (SLOTS && maybe_empty) {
-        const unsigned wk = w_first + (unsigned)k;
-        if (split_begin(wk, a.nwg, TT) == split_begin(wk + 1, a.nwg, TT)) l = -__builtin_inff();
-      }
-      lk[u] = l;
+      lk[u] = l_base[(size_t)k * l_stride];
       load8(o_base + (size_t)k * o_stride, ov[u]);
     }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) lk[u] = dead[u] ? -__builtin_inff() : lk[u] * l_scale;
+    // No branch on the loaded values: while every part so far is empty, m and
+    // mc are -inf, alpha is 0 and every weight is 0, so s and acc stay 0.
     float mc = m;
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) mc = fmaxf(mc, lk[u]);
-    if (mc != -__builtin_inff()) {
-      const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mc);
-      s *= alpha;
+    const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mc);
+    s *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const bool live = lk[u] != -__builtin_inff();  // an empty part's o is never used
-        const float wk = live ? fast_exp2(lk[u] - mc) : 0.f;
-        s += wk;
+    for (int u = 0; u < UNROLL; ++u) {
+      const bool live = lk[u] != -__builtin_inff();  // an empty part's o is never used
+      const float wk = live ? fast_exp2(lk[u] - mc) : 0.f;
+      s += wk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += live ? wk * ov[u][e] : 0.f;
-      }
-      m = mc;
+      for (int e = 0; e < 8; ++e) acc[e] += live ? wk * ov[u][e] : 0.f;
     }
+    m = mc;
   }
   // Combine the part groups (lanes dl, dl + LPR, ... hold the same dims).
   float mt = m;
