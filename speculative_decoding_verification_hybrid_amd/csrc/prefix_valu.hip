@@ -108,13 +108,29 @@ __global__ void __launch_bounds__(256) prefix_valu_kernel(ValuArgs a) {
       const bool tree = ti >= n_prefix;
       const TIn* ks = tree ? ktg + kt_off : kg + kv_off + (size_t)ti * NK * D;
       const TIn* vs = tree ? vtg + kt_off : vg + kv_off + (size_t)ti * NK * D;
-      const int nvalid = tree ? a.T : min(NK, L - ti * NK);
-      __syncthreads();
-      for (int idx = tid; idx < NK * D; idx += 256) {
+      const int nvalid = tree ? a.T : min(NK, L - ti * NK);  // >= 1 for every tile that exists
+      // All of this thread's loads of the tile are issued before the first is
+      // waited on (one memory round trip per tile, not one per element). Rows
+      // past the valid tokens read the last valid row, so every read is in
+      // bounds; they are stored as zeros.
+      constexpr int PER = NK * D / 256;
+      float kval[PER], vval[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int idx = tid + 256 * i;
+        const int tk = idx / D, d = idx % D;
+        const int src = min(tk, nvalid - 1) * D + d;
+        kval[i] = load_elem(ks + src);
+        vval[i] = load_elem(vs + src);
+      }
+      __syncthreads();  // every thread is done with the previous tile's Ks, Vs and Ps
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int idx = tid + 256 * i;
         const int tk = idx / D, d = idx % D;
         const bool ok = tk < nvalid;
-        Ks[tk * KROW + d] = ok ? load_elem(ks + idx) : 0.f;
-        Vs[tk * D + d] = ok ? load_elem(vs + idx) : 0.f;
+        Ks[tk * KROW + d] = ok ? kval[i] : 0.f;
+        Vs[tk * D + d] = ok ? vval[i] : 0.f;
       }
       __syncthreads();
       const unsigned long long vis = tree ? anc_s[node] : 0ull;
