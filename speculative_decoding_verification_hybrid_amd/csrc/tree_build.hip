@@ -141,10 +141,10 @@ struct TreeArgs {
   int* status;
 };
 
-// The split lists of sequence b merged by wave 0 into top[0 .. kk).
-__device__ void merge_top(const TreeArgs& a, int b, unsigned long long* top) {
-  if ((threadIdx.x >> 6) != 0) return;
-  constexpr int E = kMaxTreeSplit * (kMaxTreeGuesses + 1) / 64;
+// The split lists of sequence b (split * kk keys) merged by wave 0 into
+// top[0 .. kk), with E keys per lane (64 E >= split * kk).
+template <int E>
+__device__ void merge_top_e(const TreeArgs& a, int b, unsigned long long* top) {
   unsigned long long mine[E];
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -154,6 +154,21 @@ __device__ void merge_top(const TreeArgs& a, int b, unsigned long long* top) {
                                  : 0ull;
   }
   select_top_wave<E>(mine, a.kk, top);
+}
+// Every selection round scans all E keys of a lane, so E follows the actual
+// list length (a 128k vocabulary with 16 keys per split needs 8, not 32).
+__device__ void merge_top(const TreeArgs& a, int b, unsigned long long* top) {
+  if ((threadIdx.x >> 6) != 0) return;
+  static_assert(kMaxTreeSplit * (kMaxTreeGuesses + 1) <= 64 * 32, "merge list fits 32 keys per lane");
+  const int n = a.split * a.kk;
+  if (n <= 64 * 4)
+    merge_top_e<4>(a, b, top);
+  else if (n <= 64 * 8)
+    merge_top_e<8>(a, b, top);
+  else if (n <= 64 * 16)
+    merge_top_e<16>(a, b, top);
+  else
+    merge_top_e<32>(a, b, top);
 }
 
 // grid: (B, scan workgroups): workgroup c looks for the queries among the grams
