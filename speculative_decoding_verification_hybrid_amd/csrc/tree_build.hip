@@ -90,6 +90,48 @@ __device__ void select_top_wave(const unsigned long long* mine, int kk, unsigned
   }
 }
 
+// bf16 logits within one 4096-entry slice: a 32-bit key holds the 16
+// order-preserving value bits and the reversed slice index (12 bits) below,
+// with bit 28 set (0 = no key), so its order is that of make_key on the same
+// entries and the first selection runs on 32-bit compares and exchanges.
+__device__ __forceinline__ unsigned ordered16(unsigned bits16) {
+  return (bits16 & 0x8000u) ? (~bits16 & 0xffffu) : (bits16 | 0x8000u);
+}
+__device__ __forceinline__ unsigned slice_key(unsigned bits16, int local) {
+  return (1u << 28) | (ordered16(bits16) << 12) | (unsigned)(kTopChunk - 1 - local);
+}
+__device__ __forceinline__ unsigned long long slice_key_to_key(unsigned k, int lo) {
+  if (k == 0u) return 0ull;
+  const unsigned ord = (k >> 12) & 0xffffu;
+  const unsigned bits16 = (ord & 0x8000u) ? (ord & 0x7fffu) : (~ord & 0xffffu);
+  return make_key(bf16_bits_to_float(bits16), (unsigned)(lo + (kTopChunk - 1) - (int)(k & (kTopChunk - 1))));
+}
+static_assert(kTopChunk == 4096, "slice keys hold a 12-bit index");
+__device__ __forceinline__ unsigned wave_max32(unsigned k) {
+  k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x124, 0xf, 0xf, false));  // row_ror:4
+  k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x128, 0xf, 0xf, false));  // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap(k, k, false, false);
+  k = max((unsigned)r[0], (unsigned)r[1]);
+  r = __builtin_amdgcn_permlane32_swap(k, k, false, false);
+  return max((unsigned)r[0], (unsigned)r[1]);
+}
+// select_top_wave on slice keys; lane 0 writes the 64-bit keys of the winners.
+template <int E>
+__device__ void select_top_wave32(const unsigned* mine, int kk, int lo, unsigned long long* out) {
+  unsigned bound = ~0u;
+  for (int j = 0; j < kk; ++j) {
+    unsigned best = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (mine[e] < bound) best = max(best, mine[e]);
+    best = wave_max32(best);
+    if ((threadIdx.x & 63) == 0) out[j] = slice_key_to_key(best, lo);
+    bound = best;
+  }
+}
+
 // grid: B*split workgroups. Each wave selects the kk largest of its 1024 keys,
 // then wave 0 selects the kk largest of the four lists. Workgroup 0 of a
 // sequence also resets that sequence's match slots for the scan.
@@ -101,18 +143,24 @@ __global__ void __launch_bounds__(kTopThreads) topk_partial_kernel(const void* l
   const int lo = s * kTopChunk;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (s == 0 && threadIdx.x < kMaxTreeGuesses + 1) best_g[b * (kMaxTreeGuesses + 1) + threadIdx.x] = -1;
-  unsigned long long mine[kTopEPT];
+  if (BF16) {
+    unsigned mine[kTopEPT];
 #pragma unroll
-  for (int e = 0; e < kTopEPT; ++e) {
-    const int i = lo + wv * (64 * kTopEPT) + lane + e * 64;
-    float x = 0.f;
-    if (i < V) {
-      if (BF16) x = bf16_bits_to_float(static_cast<const unsigned short*>(logits)[(size_t)b * V + i]);
-      else x = static_cast<const float*>(logits)[(size_t)b * V + i];
+    for (int e = 0; e < kTopEPT; ++e) {
+      const int local = wv * (64 * kTopEPT) + lane + e * 64;
+      const int i = lo + local;
+      mine[e] = i < V ? slice_key(static_cast<const unsigned short*>(logits)[(size_t)b * V + i], local) : 0u;
     }
-    mine[e] = i < V ? make_key(x, (unsigned)i) : 0ull;
+    select_top_wave32<kTopEPT>(mine, kk, lo, wave_top[wv]);
+  } else {
+    unsigned long long mine[kTopEPT];
+#pragma unroll
+    for (int e = 0; e < kTopEPT; ++e) {
+      const int i = lo + wv * (64 * kTopEPT) + lane + e * 64;
+      mine[e] = i < V ? make_key(static_cast<const float*>(logits)[(size_t)b * V + i], (unsigned)i) : 0ull;
+    }
+    select_top_wave<kTopEPT>(mine, kk, wave_top[wv]);
   }
-  select_top_wave<kTopEPT>(mine, kk, wave_top[wv]);
   __syncthreads();
   if (wv == 0) {
     unsigned long long m2[(kTopThreads / 64) * (kMaxTreeGuesses + 1) / 64];
