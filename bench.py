@@ -16,8 +16,10 @@ eager step on the same inputs.
 Prints one JSON line. ``value`` is the layer's achieved HBM bandwidth on its
 algorithmic bytes (valid KV read once + q, tree K/V, out, lse, tree shape);
 beside it: the per-layer latency, verified tokens/s, the split-KV kernel's
-roofline (its K launches captured and timed the same way, alone) and the fp64
-CPU oracle's throughput on a bounded sample of the same workload. A second
+roofline (its K launches captured and timed the same way, alone; against the
+HBM peak, and in "mfma" against the bf16 matrix-core peak with the busy
+fractions of a committed rocprofv3 counter pass) and the fp64 CPU oracle's
+throughput on a bounded sample of the same workload. A second
 leg ("accept_commit") times hta_accept + hta_commit on the same draft tree
 with bf16 target logits over a 128256-token vocabulary, the same way, with
 the oracle's accept + commit on the same inputs beside it. A third leg
