@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhta.so")
-SOURCES = ["hta_api.hip", "prefix_mfma.hip", "prefix_mfma2.hip", "prefix_valu.hip", "tree.hip", "merge.hip",
+SOURCES = ["hta_api.hip", "prefix_mfma.hip", "prefix_valu.hip", "tree.hip", "merge.hip",
            "accept.hip", "prefix_dot.hip",
            "window.hip", "tree_build.hip"]
 ARCH = "gfx950"
@@ -31,9 +31,10 @@ CFLAGS = [
 ]
 
 
-# Per-source additions: the two-block split-KV kernel wants MFMA results in
-# VGPRs (its scores go straight into VALU softmax code).
-FILE_FLAGS = {"prefix_mfma2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source additions: the split-KV MFMA kernel wants MFMA results in VGPRs
+# (its scores go straight into the softmax; its P.V accumulators are pinned to
+# AGPRs by inline assembly).
+FILE_FLAGS = {"prefix_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def flags_for(src: str) -> list:

@@ -64,32 +64,36 @@ int validate(const hta_config_t* c) {
 }
 
 // Split-KV kernel shape. MFMA path: query rows in blocks of 32; a wave owns
-// qb blocks (qb = 1: at most 8 waves per workgroup; qb = 2: one wave per SIMD,
-// at most 4); more rows than one workgroup holds go to further row groups
-// (grid.y). The plan takes qb = 1: with a single wave per SIMD the two-block
-// kernel's instruction issue (its LDS reads in particular) is not hidden, and
-// it measures slower at the shapes benchmarked; qb = 2 is taken on request.
-// VALU path: 16 rows per workgroup. DOT path: all M <= 8 rows in one
-// workgroup of 4 waves.
+// qb blocks (one wave per SIMD, at most 4 per workgroup; 2, or 4 when fewer
+// blocks would leave a wave count that is not 1, 2 or 4); more rows than
+// one workgroup holds go to further row groups (grid.y). The plan takes qb = 2
+// whenever there are two blocks or more, so every K / V fragment read from LDS
+// feeds two MFMAs; qb = 1 is taken on request or for a single block.
+// VALU path: 16 rows per workgroup. DOT path: all M rows in one workgroup of
+// 4 waves.
 void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) {
   pl->path = path;
   if (path == HTA_PATH_MFMA) {
+    pl->tile_tokens = hta::kMfmaTileTokens;
     const int nqb = (d.M + 31) / 32;
-    const int qb = qb_req > 0 ? qb_req : 1;
-    const int nwb = (nqb + qb - 1) / qb;   // wave-sized row blocks
-    const int maxw = qb == 2 ? 4 : 8;
-    const int rg = (nwb + maxw - 1) / maxw;
-    const int per = (nwb + rg - 1) / rg;
+    const int qb = qb_req > 0 ? qb_req : (nqb >= 2 ? 2 : 1);
+    const int max_blocks = 4 * qb;              // blocks per workgroup
+    const int rg = (nqb + max_blocks - 1) / max_blocks;
+    const int per = (nqb + rg - 1) / rg;        // blocks per row group
+    int waves = (per + qb - 1) / qb;
+    waves = waves <= 1 ? 1 : waves <= 2 ? 2 : 4;
     pl->row_groups = rg;
-    pl->rows_per_group = per * 32 * qb;
-    pl->waves = per;
+    pl->rows_per_group = per * 32;
+    pl->waves = waves;
     pl->qb = qb;
   } else if (path == HTA_PATH_DOT) {
+    pl->tile_tokens = hta::kTileTokens;
     pl->row_groups = 1;
     pl->rows_per_group = d.M;
     pl->waves = 4;
     pl->qb = 0;
   } else {
+    pl->tile_tokens = hta::kTileTokens;
     pl->row_groups = (d.M + 15) / 16;
     pl->rows_per_group = 16;
     pl->waves = 4;
@@ -174,12 +178,12 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   if (nwg <= 0) {
     nwg = (int64_t)cus * (occ > 0 ? occ : 1) / h->pl.row_groups;
     nwg = nwg < 8 ? 8 : (nwg / 8) * 8;
-    const int64_t tiles = (int64_t)d.B * d.Hkv * ((d.Lcap + hta::kTileTokens - 1) / hta::kTileTokens + 1);
-    if (nwg > tiles) nwg = tiles;
   }
   // The kernels split tiles with 32-bit arithmetic: keep max_tiles * nwg < 2^32.
+  const int nk = h->pl.tile_tokens;
   const int64_t max_tiles =
-      (int64_t)d.B * d.Hkv * ((d.Lcap + hta::kTileTokens - 1) / hta::kTileTokens + 1);
+      (int64_t)d.B * d.Hkv * ((d.Lcap + nk - 1) / nk + hta::tree_tiles_for(d.T, nk));
+  if (cfg->num_workgroups <= 0 && nwg > max_tiles) nwg = max_tiles;
   const int64_t nwg_cap = (int64_t)UINT32_MAX / max_tiles;
   if (nwg_cap < 1) {
     delete h;
@@ -237,7 +241,7 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   p.rows_per_group = h->pl.rows_per_group;
   p.waves_per_workgroup = h->pl.waves;
   p.qblocks_per_wave = h->pl.qb;
-  p.tile_tokens = hta::kTileTokens;
+  p.tile_tokens = h->pl.tile_tokens;
   p.max_slots = (int32_t)max_slots;
   p.workspace_bytes = (int64_t)off;
   p.device = dev;
@@ -273,8 +277,9 @@ int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hta::PrefixInputs in = {q, k_cache, v_cache, k_tree, v_tree, parent, prefix_len};
   HTA_TRY(launch_split(h, in, s));
-  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, 1, prefix_len, h->slots, h->err_b, out,
-                                           h->dims.bf16, lse, h->status, s));
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg,
+                                           hta::tree_tiles_for(h->dims.T, h->pl.tile_tokens), prefix_len, h->slots,
+                                           h->err_b, out, h->dims.bf16, lse, h->status, s));
 }
 
 int hta_cross_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
@@ -284,8 +289,8 @@ int hta_cross_attn(hta_handle_t h, const void* q, const void* k_cache, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hta::PrefixInputs in = {q, k_cache, v_cache, nullptr, nullptr, nullptr, prefix_len};
   HTA_TRY(launch_split(h, in, s));
-  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, 0, prefix_len, h->slots, nullptr, out,
-                                           h->dims.bf16, lse, h->status, s));
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg, 0, prefix_len, h->slots,
+                                           nullptr, out, h->dims.bf16, lse, h->status, s));
 }
 
 int hta_window_attn(hta_handle_t h, const void* q, const void* k_ring, const void* v_ring, const void* k_new,
@@ -365,8 +370,9 @@ int hta_merge_prefix(hta_handle_t h, const int32_t* prefix_len, float* o_prefix,
                      void* stream) {
   if (!h || !prefix_len || !o_prefix || !lse_prefix) return HTA_ERR_INVALID_ARG;
   if (!all_aligned(o_prefix)) return HTA_ERR_INVALID_ARG;
-  return check_hip(hta::launch_merge_slots(h->dims, h->pl.nwg, 0, prefix_len, h->slots, nullptr, o_prefix,
-                                           false, lse_prefix, h->status, static_cast<hipStream_t>(stream)));
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg, 0, prefix_len, h->slots,
+                                           nullptr, o_prefix, false, lse_prefix, h->status,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int hta_lse_merge(hta_handle_t h, int32_t n_parts, const float* o_parts, const float* lse_parts,

@@ -7,7 +7,11 @@
 
 namespace hta {
 
-constexpr int kTileTokens = 64;  // prefix tokens per pipeline stage (both prefix paths)
+constexpr int kTileTokens = 64;      // prefix tokens per tile of the split (VALU and DOT paths)
+constexpr int kMfmaTileTokens = 32;  // prefix tokens per tile of the split (MFMA path)
+
+// Tiles that hold a segment's T tree tokens when the tree part is fused in.
+__host__ __device__ inline int tree_tiles_for(int T, int nk) { return (T + nk - 1) / nk; }
 
 struct Dims {
   int B, Hq, Hkv, G, T, D, Lcap, M;  // M = G*T query rows per KV head
@@ -25,7 +29,8 @@ struct Slots {
 };
 
 struct PrefixLaunch {
-  int path;           // 1 MFMA, 2 VALU
+  int path;           // 1 MFMA, 2 VALU, 3 DOT
+  int tile_tokens;    // tokens per tile of the split
   int nwg;            // workgroups per row group
   int row_groups;     // grid.y
   int rows_per_group; // multiple of 32 (MFMA) or of 16 (VALU)
@@ -34,8 +39,9 @@ struct PrefixLaunch {
 };
 
 // Inputs of the split-KV kernels. With k_tree/v_tree/parent set, each
-// (sequence, KV head) gets one extra tile of tree tokens under the ancestor
-// mask (the fused tree part); with them null only the cached part is done.
+// (sequence, KV head) gets tree_tiles_for(T, tile_tokens) extra tiles of tree
+// tokens under the ancestor mask (the fused tree part); with them null only
+// the cached part is done.
 struct PrefixInputs {
   const void* q;
   const void* k_cache;
@@ -95,10 +101,11 @@ hipError_t launch_tree_attn(const Dims& d, const void* q, const void* k_tree, co
 hipError_t launch_tree_mask(const Dims& d, const int* parent, uint64_t* mask_out, int* status,
                             hipStream_t s);
 
-// Merge of the slots of one split-KV launch (tree_tiles as in that launch)
-// into out (float or bf16) and natural-log lse; err_b (may be null) marks
-// sequences whose rows become NaN.
-hipError_t launch_merge_slots(const Dims& d, int nwg, int tree_tiles, const int* prefix_len, Slots slots,
+// Merge of the slots of one split-KV launch (tile_tokens, nwg and
+// tree_tiles as in that launch) into out (float or bf16) and natural-log
+// lse; err_b (may be null) marks sequences whose rows become NaN.
+hipError_t launch_merge_slots(const Dims& d, int tile_tokens, int nwg, int tree_tiles, const int* prefix_len,
+                              Slots slots,
                               const int* err_b, void* out, bool out_bf16, float* lse, int* status,
                               hipStream_t s);
 // Merge of n_parts caller-provided partials (natural-log LSE) into float out.

@@ -18,7 +18,6 @@
 namespace hta {
 namespace {
 
-constexpr int NK = kTileTokens;
 constexpr int UNROLL = 8;
 
 struct MergeArgs {
@@ -28,7 +27,7 @@ struct MergeArgs {
   const float* slot_lse2;
   const int* err_b;
   int* status;
-  int nwg, tree_tiles;
+  int nk, nwg, tree_tiles;
   // parts mode: n_parts caller arrays, natural-log lse
   const float* o_parts;
   const float* lse_parts;
@@ -94,7 +93,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
 #pragma unroll 4
     for (int bb = 0; bb < a.B; ++bb) {
       const int Lb = a.prefix_len[bb];
-      const int nt = tiles_of((Lb < 0 || Lb > a.Lcap) ? 0 : Lb, NK) + a.tree_tiles;
+      const int nt = tiles_of((Lb < 0 || Lb > a.Lcap) ? 0 : Lb, a.nk) + a.tree_tiles;
       seq_tiles += (unsigned)nt;
       if (bb < b) before += (unsigned)nt;
       if (bb == b) {
@@ -249,8 +248,8 @@ unsigned grid_for(const Dims& d) {
 
 }  // namespace
 
-hipError_t launch_merge_slots(const Dims& d, int nwg, int tree_tiles, const int* prefix_len, Slots slots,
-                              const int* err_b, void* out, bool out_bf16, float* lse, int* status,
+hipError_t launch_merge_slots(const Dims& d, int tile_tokens, int nwg, int tree_tiles, const int* prefix_len,
+                              Slots slots, const int* err_b, void* out, bool out_bf16, float* lse, int* status,
                               hipStream_t s) {
   MergeFn k;
   if (slots.o_bf16)
@@ -264,6 +263,7 @@ hipError_t launch_merge_slots(const Dims& d, int nwg, int tree_tiles, const int*
   a.slot_lse2 = slots.lse2;
   a.err_b = err_b;
   a.status = status;
+  a.nk = tile_tokens;
   a.nwg = nwg;
   a.tree_tiles = tree_tiles;
   a.out = out;

@@ -6,55 +6,60 @@
 // masked); the parts are combined with the log-sum-exp trick. Here the G
 // query heads that share a KV head and the T tree nodes form M = G*T query
 // rows per KV head, so one pass over the KV serves all M rows. Each
-// workgroup streams one contiguous range of 64-token tiles (see common.h) and
+// workgroup streams one contiguous range of 32-token tiles (see common.h) and
 // leaves a normalised partial (o, log2-LSE) per row in a workspace slot for
 // the merge kernel. When the tree part is fused in, each (sequence, KV head)
-// ends with one extra tile holding its tree keys/values, scored under the
-// ancestor mask built in LDS from parent[] -- the same online softmax then
-// covers both parts, and the merge combines the pieces.
+// ends with ceil(T/32) extra tiles holding its tree keys/values, scored under
+// the ancestor mask built in LDS from parent[] -- the same online softmax
+// then covers both parts, and the merge combines the pieces.
+//
+// Work per wave: one wave per SIMD, each owning QB blocks of 32 query rows
+// (64 rows at QB = 2), so every K or V fragment read from LDS feeds QB MFMAs.
+// A tile is processed in NSLOT "slots", each one MFMA plus the VALU work of
+// one or two probabilities plus at most one or two LDS reads; tile j's slots
+// run, in this order,
+//   * P.V of tile j-1 (its V^T fragments and bf16 probabilities are already
+//     in registers) while the K fragments of tile j+1 are read,
+//   * the scores of tile j+1 (S^T = K . Q^T) while the V^T fragments of tile j
+//     are read,
+// and alongside both, the softmax of tile j (its scores were computed during
+// tile j-1). The MFMA pipe therefore always has independent work queued
+// under the exp/sum of the softmax, and every LDS read has at least half a
+// tile of slots to land before its MFMA. Slots are fenced with
+// sched_barrier so the compiler keeps this composition.
 //
 // Memory pipeline: K and V tiles go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no staging registers), through 4 LDS stages, so up
-// to 3 tiles (96 KB at D = 128) are in flight per workgroup while one is
-// consumed. Each wave waits for its own copies (vmcnt), then all waves meet at
-// one barrier per tile, after which the stage of the tile just finished is
-// refilled. The copies are issued from inline assembly, so the compiler's wait
-// insertion never sees them (it would otherwise drain the whole copy queue
-// before LDS reads it cannot prove disjoint from a copy in flight); every wait
-// on them is explicit (the Q fragments are loaded the same way, just before
-// the first copies of a piece).
+// global_load_lds_dwordx4 (no staging registers) through NS stages of 16 KB
+// (D = 128). Tile j's K fragments are read during tile j-1 and its V
+// fragments during tile j, and its V registers are consumed during tile j+1,
+// so at the start of tile j the stage of tile j-2 is free everywhere: after
+// one workgroup barrier (which also publishes every wave's copies of tile
+// j+1) it is refilled with tile j-2+NS, leaving NS-3 tiles in flight. Each
+// wave waits for its own copies with an explicit vmcnt; the copies (and the Q
+// loads, queued ahead of them) come from inline assembly so the compiler's
+// wait insertion never drains the copy queue before an LDS read.
 //
-// One copy instruction moves 1 KB: 4 (D = 128) or 8 (D = 64) whole rows of K
-// or V, read coalesced from HBM, with the lanes' 16-byte chunks permuted on
-// the way into LDS. K rows keep their 16-byte chunks XOR-swizzled by row; V is
-// stored as 128-byte blocks of 4 tokens x 16 dims, which is exactly what one
-// 16-lane group of a transposed read consumes.
+// Layouts: K rows keep their 16-byte chunks XOR-swizzled by row
+// (conflict-free ds_read_b128 for the MFMA A operand); V is stored as
+// 128-byte blocks of 4 tokens x 16 dims, exactly what one 16-lane group of
+// ds_read_b64_tr_b16 consumes. Both come from permuting which global 16-byte
+// chunk each lane of a copy fetches; the global side stays coalesced.
 //
-// Compute: WQ waves (two per SIMD at WQ = 8), each owning one block of 32
-// query rows; the first wave of each SIMD runs at higher priority, so the pair
-// drifts into alternating MFMA and softmax phases.
-//   * scores are computed transposed, S^T = K . Q^T: each lane holds one
-//     query row (a column of the MFMA result) and 16 tokens, so the row max
-//     needs one cross-half exchange and the running (m, l) live in lanes;
-//   * K rows are fed to the MFMA with bits 2 and 3 of the row index swapped,
-//     which makes the 8 scores a half-wave holds for each 16-token k-chunk
-//     belong to 8 consecutive tokens; converted to bf16 they are directly the
-//     B operand of O^T += V^T . P^T;
-//   * the V^T operand comes from ds_read_b64_tr_b16: in each 16-lane group,
-//     lane i receives element i%4 of the 8-byte chunks read by lanes
-//     4j + i/4 (j = 0..3), so lanes that read 4 dims of 4 consecutive tokens
-//     hand each lane 4 consecutive tokens of one dim.
-// LDS reads run ahead of their use: the V fragments of a 32-token sub-tile
-// are read while its score MFMAs run, and the K fragments of the next
-// sub-tile while the softmax runs.
-// Online softmax runs in the log2 domain with a lazily updated maximum: the
-// stored max only moves when a sub-tile's max exceeds it by more than 8 (so
-// exp2 stays below 256), which is exact because the same stale max is used
-// for both the sum and the output. The row max itself is only computed when
-// the probabilities against the stored max sum to more than 256 (the sum
-// bounds every term), which after the first sub-tile is rare.
-#include <type_traits>
-
+// MFMA mapping: scores are computed transposed, so each lane holds one query
+// row (a column of the result) and 16 tokens; the row max needs one
+// cross-half exchange and the running (m, l) live in lanes. K rows are fed
+// with bits 2 and 3 of the row index swapped, which makes the 8 scores a
+// half-wave holds per 16-token k-chunk belong to 8 consecutive tokens:
+// converted to bf16 they are directly the B operand of O^T += V^T . P^T.
+// The V^T operand comes from the transposed LDS read.
+//
+// Online softmax in the log2 domain with a lazily updated maximum: the stored
+// max m only moves when a tile's max exceeds it by more than 8 (so each
+// probability stays below 256), which is exact because the same stale max is
+// used for both the sum and the output. The row max itself is only computed
+// when the probabilities against the stored max sum to more than 256 (the
+// sum bounds every term) or m is still -inf, which after a piece's first tile
+// is rare; that check sits after the slots, where it also rescales O.
 #include "hta_internal.h"
 #include "prefix_mfma_common.h"
 
@@ -62,30 +67,93 @@ namespace hta {
 namespace mfma {
 namespace {
 
-// Threads per workgroup: the WQ compute waves plus copy-only waves up to 4
-// (WQ <= 4) or 8.
-template <int WQ>
-constexpr int threads_for() { return WQ <= 4 ? 256 : 512; }
+// Static schedule of one tile's slots (see the header comment): slot k
+// issues one MFMA (P.V for k < NPV, then scores), then its LDS reads. The
+// reads are spread so that no slot asks the LDS for much more than the MFMA
+// takes: the KC K fragments of the next tile evenly over the P.V slots (a
+// score MFMA reads its fragment at least NPV/2 slots later), the 4*DB halves
+// of V^T fragments of this tile evenly over the score slots (after the last
+// P.V MFMA of the old fragment, at least NSC/2 slots before the next tile's
+// first use). kwait(c) is the lgkmcnt that covers K fragment c at its first
+// score MFMA.
+template <int D, int QB>
+struct SlotSchedule {
+  static constexpr int KC = D / 16, DB = D / 32, NPV = 2 * DB * QB, NSC = KC * QB, NSLOT = NPV + NSC;
+  static constexpr int kslot(int c) { return c * NPV / KC; }
+  static constexpr int vslot(int f, int h) { return NPV + (2 * f + h) * NSC / (4 * DB); }
+  static constexpr int nv_in(int s) {
+    int n = 0;
+    for (int f = 0; f < 2 * DB; ++f)
+      for (int h = 0; h < 2; ++h) n += vslot(f, h) == s;
+    return n;
+  }
+  static constexpr int nk_in(int s) {
+    int n = 0;
+    for (int c = 0; c < KC; ++c) n += kslot(c) == s;
+    return n;
+  }
+  static constexpr int ops_before(int s) {
+    int n = 0;
+    for (int t = 0; t < s; ++t) n += nv_in(t) + nk_in(t);
+    return n;
+  }
+  // index of K read c in issue order (a slot issues its V reads, then its K
+  // reads in order of c)
+  static constexpr int kidx(int c) {
+    int n = ops_before(kslot(c)) + nv_in(kslot(c));
+    for (int e = 0; e < c; ++e) n += kslot(e) == kslot(c);
+    return n;
+  }
+  static constexpr int kwait(int c) { return ops_before(NPV + c * QB) - kidx(c) - 1; }
+  // index of the read of half h of V fragment f in issue order (the V reads
+  // of a slot in order of (f, h))
+  static constexpr int vidx(int f, int h) {
+    int n = ops_before(vslot(f, h));
+    for (int g = 0; g < 2 * DB; ++g)
+      for (int e = 0; e < 2; ++e)
+        if ((g < f || (g == f && e < h)) && vslot(g, e) == vslot(f, h)) ++n;
+    return n;
+  }
+  // lgkmcnt that covers V fragment f (read during the previous tile) at its
+  // first P.V MFMA, slot f*QB: the reads issued after it in the previous tile
+  // plus this tile's reads before that slot.
+  static constexpr int vwait(int f) { return ops_before(NSLOT) - vidx(f, 1) - 1 + ops_before(f * QB); }
+  static constexpr bool valid() {
+    for (int f = 0; f < 2 * DB; ++f)
+      if (vslot(f, 1) >= NSLOT || vslot(f, 0) < (f + 1) * QB) return false;
+    for (int c = 0; c < KC; ++c)
+      if (kslot(c) >= NPV + c * QB || kwait(c) < 0) return false;
+    for (int f = 0; f < 2 * DB; ++f)
+      if (vwait(f) < 0) return false;
+    return true;
+  }
+  static_assert(valid(), "slot schedule");
+};
 
-template <int D, int WQ>
-__global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixArgs a) {
-  constexpr int NWAVE = threads_for<WQ>() / 64;
-  constexpr int KC = D / 16;          // k-chunks of K.Q^T
-  constexpr int DB = D / 32;          // 32-dim blocks of O
-  constexpr int DCH = D / 8;          // 16-byte chunks per row
-  constexpr int DG = D / 16;          // 16-dim groups (V blocks per 4 tokens)
-  constexpr int TILE = NK * D;        // bf16 elements of one K (or V) tile
-  constexpr int STAGE = 2 * TILE;     // K tile, then V tile
-  constexpr int RPB = 64 / DCH;       // rows per 1 KB copy block
-  constexpr int NBLK = NK / RPB;      // copy blocks per K (or V) tile
-  constexpr int NBH = NBLK / NWAVE;   // K (and V) copy instructions per wave per tile
-  constexpr int GRP = 2 * NBH;        // copy instructions per wave per tile
-  constexpr int SROW = D + 8;         // epilogue staging row (16-byte aligned rows)
-  static_assert(NBLK % NWAVE == 0, "copy blocks split evenly over the waves");
-  static_assert(NSTAGE * STAGE >= NWAVE * 32 * SROW, "epilogue staging fits in the tile buffers");
-  static_assert(3 * GRP < 64, "vmcnt range");
+template <int D, int QB, int NWAVE, int NS>
+__global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
+  constexpr int KC = D / 16;               // 16-dim k-chunks of S^T = K.Q^T
+  constexpr int DB = D / 32;               // 32-dim blocks of O^T
+  constexpr int DCH = D / 8;               // 16-byte chunks per row
+  constexpr int DG = D / 16;               // 16-dim groups (V blocks per 4 tokens)
+  constexpr int TILE = NK * D;             // bf16 elements of one K (or V) tile
+  constexpr int STAGE = 2 * TILE;          // K tile, then V tile
+  constexpr int RPB = 64 / DCH;            // rows per 1 KB copy
+  constexpr int NBLK = NK / RPB;           // copies per K (or V) tile
+  constexpr int KPW = NBLK / NWAVE;        // K (and V) copies per wave per tile
+  constexpr int CPW = 2 * KPW;             // copies per wave per tile
+  constexpr int SROW = D + 8;              // epilogue staging row (16-byte aligned)
+  constexpr int NPV = 2 * DB * QB;         // P.V MFMAs per tile
+  constexpr int NSC = KC * QB;             // score MFMAs per tile
+  constexpr int NSLOT = NPV + NSC;
+  constexpr int EPS = 16 * QB / NSLOT;     // probabilities per slot
+  using Sch = SlotSchedule<D, QB>;
+  static_assert(NBLK % NWAVE == 0, "copies split evenly over the waves");
+  static_assert(EPS * NSLOT == 16 * QB, "slot layout");
+  static_assert(NS >= 4, "stages: tiles j-1, j, j+1 in use plus one in flight");
+  static_assert(NS * STAGE >= NWAVE * 32 * QB * SROW, "epilogue staging fits in the tile buffers");
 
-  __shared__ __attribute__((aligned(1024))) unsigned short lds[NSTAGE * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned short lds[NS * STAGE];
   __shared__ int par_s[64];
   __shared__ unsigned long long anc_s[64];
   __shared__ int bad_s;
@@ -97,7 +165,6 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
   const int l32 = lane & 31;
   const int grp = lane >> 4;  // 16-lane group (transposed V reads)
   const int gl = lane & 15;
-  if (NWAVE == 8 && wave < 4) __builtin_amdgcn_s_setprio(2);
 
   const int w = xcd_remap(blockIdx.x, a.nwg);
   const unsigned TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles);
@@ -108,41 +175,57 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
   SegmentWalk sw;
   if (!walk_start(&sw, x, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles)) return;
 
-  const bool computes = wave < WQ;  // copy-only waves issue copies and meet the barriers
-  const int row = blockIdx.y * a.rows_per_group + wave * 32 + l32;  // this lane's query row
   const int row_limit = min(a.M, (int)(blockIdx.y + 1) * a.rows_per_group);
-  const bool row_ok = computes && row < row_limit;
-  const int node = row_ok ? row % a.T : 0;
+  const int wrow0 = blockIdx.y * a.rows_per_group + wave * 32 * QB;  // first row of this wave
+  int rowq[QB];
+  bool okq[QB];
+#pragma unroll
+  for (int X = 0; X < QB; ++X) {
+    rowq[X] = wrow0 + 32 * X + l32;
+    okq[X] = rowq[X] < row_limit;
+  }
 
   // Lane-constant LDS offsets (elements, within a stage). K: the fragments of
-  // this lane's row; the swizzle depends only on the row's low 4 bits, which
-  // are the same in both 32-token sub-tiles.
-  int koff[KC];
+  // this lane's MFMA row; the swizzle depends only on the row's low 4 bits.
+  const unsigned lds_base = lds_addr(lds);
+  unsigned kaddr[KC];  // LDS byte address of K fragment c in stage 0
   {
     const int kr = kperm(l32);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) koff[c] = kr * D + (((2 * c + hh) ^ swz<D>(kr)) << 3);
+    for (int c = 0; c < KC; ++c) kaddr[c] = lds_base + (unsigned)(kr * D + (((2 * c + hh) ^ swz<D>(kr)) << 3)) * 2u;
   }
   // V block (4 tokens x 16 dims, 64 elements) of tokens 4u.., dims 16g..: (u * DG + g) * 64.
-  // A transposed read of tokens 32st + 16kc + 8hh + 4rr, dims 32db + 16(grp&1) + 0..15
-  // reads block ((8st + 4kc + 2hh + rr) * DG + 2db + (grp&1)), lane gl at 4 gl.
-  const int voff = TILE + (2 * hh * DG + (grp & 1)) * 64 + 4 * gl;
-  // This lane's part of a 1 KB copy block. K: row within the block and logical
-  // chunk. V: token within the block and dims (the V block layout above).
+  // A transposed read of tokens 16kc + 8hh + 4rr, dims 32db + 16(grp&1) + 0..15
+  // reads block ((4kc + 2hh + rr) * DG + 2db + (grp&1)), lane gl at 4 gl.
+  const unsigned voff_b = (unsigned)(TILE + (2 * hh * DG + (grp & 1)) * 64 + 4 * gl) * 2u;  // bytes
+  // This lane's part of a 1 KB copy. K: row within the copy and logical chunk.
+  // V: token within the copy and dims (the V block layout above).
+  // Copy i < KPW of a wave moves K rows (wave + i*NWAVE)*RPB .. +RPB-1 of the
+  // tile, copy KPW + i the same V rows; for a full tile, each lane's byte
+  // offsets into the tile's K and V rows (kofs, vofs) are fixed, and so is the
+  // LDS offset of each copy relative to the stage (wave part in wlds).
   const int cp_row = lane / DCH;
   const int cp_kc = lane % DCH;
   const int cp_vt = ((lane >> 3) / DG) * 4 + ((lane & 7) >> 1);
   const int cp_vd = ((lane >> 3) % DG) * 16 + (lane & 1) * 8;
+  unsigned kofs[KPW], vofs[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int r0 = (wave + i * NWAVE) * RPB;
+    kofs[i] = (unsigned)((r0 + cp_row) * D + ((cp_kc ^ swz<D>(r0 + cp_row)) << 3)) * 2u;
+    vofs[i] = (unsigned)((r0 + cp_vt) * D + cp_vd) * 2u;
+  }
+  const unsigned wlds = __builtin_amdgcn_readfirstlane(lds_base + (unsigned)(wave * RPB * D * 2));
 
   while (true) {
     const int b = sw.b, g = sw.g;
     const unsigned s_first = sw.seq_first + (unsigned)(g * sw.nt);
     const int tile0 = (int)(x - s_first);
     const unsigned piece_end = min(x_end, s_first + (unsigned)sw.nt);
-    const int ntiles = (int)(piece_end - x);
+    const int n = (int)(piece_end - x);  // tiles of this piece
     const int L = valid_prefix(a.prefix_len, b, a.Lcap);
-    const int n_prefix = sw.nt - a.tree_tiles;  // tiles of cached KV; the tree tile (if any) follows
-    const bool has_tree = a.tree_tiles && tile0 + ntiles > n_prefix;
+    const int n_prefix = sw.nt - a.tree_tiles;  // tiles of cached KV; the tree tiles (if any) follow
+    const bool has_tree = a.tree_tiles && tile0 + n > n_prefix;
     const int slot = w + b * a.Hkv + g;
     const size_t kv_off = (size_t)(b * a.Hkv + g) * (size_t)a.Lcap * D;
     const unsigned short* kp = a.k + kv_off;
@@ -150,7 +233,9 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
     const size_t kt_off = (size_t)(b * a.Hkv + g) * a.T * D;
     const unsigned short* qp = a.q + (size_t)(b * a.Hq + g * a.G) * a.T * D;
 
-    unsigned long long anc_row = 0ull;
+    unsigned long long anc[QB];
+#pragma unroll
+    for (int X = 0; X < QB; ++X) anc[X] = 0ull;
     if (has_tree) {
       if (tid == 0) bad_s = 0;
       if (tid < a.T) par_s[tid] = a.parent[(size_t)b * a.T + tid];
@@ -161,225 +246,447 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
         if (!ok) bad_s = 1;
       }
       __syncthreads();
-      anc_row = anc_s[node];
+#pragma unroll
+      for (int X = 0; X < QB; ++X) anc[X] = anc_s[okq[X] ? rowq[X] % a.T : 0];
     }
 
-    // Q^T fragments (B operand of S^T = K.Q^T): row `row`, dims 16c + 8hh .. +7.
+    // Tokens of tile t of the piece that hold keys (>= 1 for every tile).
+    auto nvalid_of = [&](int t) __attribute__((always_inline)) {
+      const int ti = tile0 + t;
+      return ti >= n_prefix ? min(NK, a.T - (ti - n_prefix) * NK) : min(NK, L - ti * NK);
+    };
+    // Queue the copies of tile t of the piece into stage t % NS: this wave's
+    // CPW of the tile's 2*NBLK 1 KB blocks (K blocks first, then V). Rows past
+    // the tile's valid tokens repeat its last valid row, so every value read
+    // is finite and in bounds; their scores are masked to -inf.
+    auto copy_tile = [&](int t) __attribute__((always_inline)) {
+      const int ti = tile0 + t;
+      const bool tree = ti >= n_prefix;
+      const size_t row0 = tree ? (size_t)(ti - n_prefix) * NK : (size_t)ti * NK;
+      const unsigned short* ks = (tree ? a.kt + kt_off : kp) + row0 * D;
+      const unsigned short* vs = (tree ? a.vt + kt_off : vp) + row0 * D;
+      const int last = nvalid_of(t) - 1;
+      const unsigned sb = wlds + (unsigned)((t % NS) * STAGE * 2);
+      static_for<0, KPW>([&](auto ii) __attribute__((always_inline)) {
+        constexpr int i = decltype(ii)::value;
+        const int r0 = (wave + i * NWAVE) * RPB;
+        const int r = r0 + cp_row;
+        copy16_to_lds_at<i * NWAVE * RPB * D * 2>(ks, (unsigned)(min(r, last) * D + ((cp_kc ^ swz<D>(r)) << 3)) * 2u,
+                                                 sb);
+      });
+      static_for<0, KPW>([&](auto ii) __attribute__((always_inline)) {
+        constexpr int i = decltype(ii)::value;
+        const int r0 = (wave + i * NWAVE) * RPB;
+        copy16_to_lds_at<(TILE + i * NWAVE * RPB * D) * 2>(vs, (unsigned)(min(r0 + cp_vt, last) * D + cp_vd) * 2u,
+                                                          sb);
+      });
+    };
+    // The same for a full prefix tile whose K / V rows start at ks / vs, into
+    // the stage at LDS byte offset sb (every offset precomputed).
+    auto copy_full = [&](const unsigned short* ks, const unsigned short* vs, unsigned sb)
+                         __attribute__((always_inline)) {
+      static_for<0, KPW>([&](auto ii) __attribute__((always_inline)) {
+        constexpr int i = decltype(ii)::value;
+        copy16_to_lds_at<i * NWAVE * RPB * D * 2>(ks, kofs[i], sb);
+      });
+      static_for<0, KPW>([&](auto ii) __attribute__((always_inline)) {
+        constexpr int i = decltype(ii)::value;
+        copy16_to_lds_at<(TILE + i * NWAVE * RPB * D) * 2>(vs, vofs[i], sb);
+      });
+    };
+    // Wait until at most `ahead` tiles' copies of this wave are in flight.
+    auto wait_ahead = [&](int ahead) __attribute__((always_inline)) {
+      switch (ahead) {
+#define HTA_WAIT_CASE(k) \
+  case k: __builtin_amdgcn_s_waitcnt(vmcnt_only<(k * CPW < 63 ? k * CPW : 63)>()); break;
+        HTA_WAIT_CASE(1) HTA_WAIT_CASE(2) HTA_WAIT_CASE(3) HTA_WAIT_CASE(4) HTA_WAIT_CASE(5)
+        HTA_WAIT_CASE(6) HTA_WAIT_CASE(7) HTA_WAIT_CASE(8) HTA_WAIT_CASE(9) HTA_WAIT_CASE(10)
+#undef HTA_WAIT_CASE
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_only<0>()); break;
+      }
+    };
+    static_assert(NS - 2 <= 10, "wait_ahead cases");
+
+    // Hidden scores of tile t (tree tile, ragged last prefix tile) get -inf
+    // added. Sc[X][v] scores token 16*(v/8) + 8*hh + v%8 of the tile.
+    auto mask_scores = [&](f32x16* Sc, int t) __attribute__((always_inline)) {
+      const int ti = tile0 + t;
+      const bool tree = ti >= n_prefix;
+      const int nv = nvalid_of(t);
+      if (tree || nv < NK) {
+        const int j0 = 8 * hh;
+        const int n0 = min(max(nv - j0, 0), 8), n1 = min(max(nv - j0 - 16, 0), 8);
+        const unsigned lim = ((1u << n0) - 1u) | (((1u << n1) - 1u) << 8);
+        const int tb = tree ? (ti - n_prefix) * NK + j0 : 0;
+#pragma unroll
+        for (int X = 0; X < QB; ++X) {
+          unsigned vis = lim;
+          if (tree)
+            vis &= (unsigned)((anc[X] >> tb) & 0xffull) | ((unsigned)((anc[X] >> (tb + 16)) & 0xffull) << 8);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) Sc[X][v] += __uint_as_float((((vis >> v) & 1u) - 1u) & 0xff800000u);
+        }
+      }
+    };
+
+    f32x16 O[QB][DB];
+    f32x16 S[QB];
+    bf16x8 P[QB][2], vf[2][DB];
+    float m[QB], l[QB];
+#pragma unroll
+    for (int X = 0; X < QB; ++X) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) O[X][db][v] = 0.f;
+      m[X] = -__builtin_inff();
+      l[X] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) P[X][kc][e] = (__bf16)0.f;
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[kc][db][e] = (__bf16)0.f;
+
+    // Prologue: queue tile 0, the Q loads and tile 1 only, wait for tile 0
+    // and Q, score tile 0. Every CU asking for all its stages at once (every
+    // workgroup does this at the same moment) would keep its waves blocked on
+    // issuing copies until most of those bytes had arrived; the other stages
+    // are filled during the first tiles instead (two tiles per tile until the
+    // ring is full).
+    constexpr int P0 = 2;
+    copy_tile(0);
+    // Q^T fragments (B operand of S^T = K.Q^T): row rowq[X], dims 16c + 8hh .. +7.
     // Loaded from inline assembly, like the tile copies, so that one explicit
-    // wait covers both: they are queued before the first tiles' copies and are
-    // complete once tile 0 is. Rows past the limit load row 0 and are zeroed.
-    bf16x8 qf[KC];
-    {
-      const unsigned short* qr = qp + (size_t)(row_ok ? row : 0) * D + 8 * hh;
+    // wait covers both: they are queued right after tile 0's copies and are
+    // complete once every copy queued before tile 1's is. Rows past the limit
+    // load row 0 and are zeroed.
+    bf16x8 qf[QB][KC];
+#pragma unroll
+    for (int X = 0; X < QB; ++X) {
+      const unsigned short* qr = qp + (size_t)(okq[X] ? rowq[X] : 0) * D + 8 * hh;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         u32x4 r;
         asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(qr + 16 * c) : "memory");
-        qf[c] = __builtin_bit_cast(bf16x8, r);
+        qf[X][c] = __builtin_bit_cast(bf16x8, r);
       }
     }
-    // Queue the copies of tile t of the piece into stage t % NSTAGE: this
-    // wave's NBH blocks of K and NBH blocks of V. Rows past the tile's valid
-    // tokens repeat its last valid row, so every value read is finite and in
-    // bounds; their scores are masked to -inf.
-    auto copy_tile = [&](int t) __attribute__((always_inline)) {
-      const int ti = tile0 + t;
-      const bool tree = ti >= n_prefix;
-      const unsigned short* ks = tree ? a.kt + kt_off : kp + (size_t)ti * NK * D;
-      const unsigned short* vs = tree ? a.vt + kt_off : vp + (size_t)ti * NK * D;
-      const int last = (tree ? a.T : min(NK, L - ti * NK)) - 1;
-      unsigned short* dst = lds + (t % NSTAGE) * STAGE;
-#pragma unroll
-      for (int i = 0; i < NBH; ++i) {
-        const int r0 = (wave + i * NWAVE) * RPB;  // first row of the block (wave-uniform)
-        const int r = r0 + cp_row;
-        copy16_to_lds(ks, (unsigned)(min(r, last) * D + ((cp_kc ^ swz<D>(r)) << 3)) * 2u,
-                      lds_addr(dst + r0 * D));
-      }
-#pragma unroll
-      for (int i = 0; i < NBH; ++i) {
-        const int r0 = (wave + i * NWAVE) * RPB;
-        copy16_to_lds(vs, (unsigned)(min(r0 + cp_vt, last) * D + cp_vd) * 2u, lds_addr(dst + TILE + r0 * D));
-      }
-    };
-    // Wait until at most n tiles' copies of this wave are still in flight.
-    auto wait_tiles = [&](int n) __attribute__((always_inline)) {
-      if (n >= 3)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<3 * GRP>());
-      else if (n == 2)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<2 * GRP>());
-      else if (n == 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<GRP>());
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
-    };
-
-    f32x16 O[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) O[db][v] = 0.f;
-    float m = -__builtin_inff(), l = 0.f;
-
-    bf16x8 ka[KC];
-    auto load_k = [&](const unsigned short* kb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int c = 0; c < KC; ++c) ka[c] = *(const bf16x8*)(kb + koff[c]);
-    };
-
-    // Every stage starts filled: tile t goes to stage t % NSTAGE, and the stage
-    // of tile t is refilled (with tile t + NSTAGE) once tile t is consumed.
-    for (int t = 0; t < min(ntiles, NSTAGE); ++t) copy_tile(t);
-    wait_tiles(min(ntiles, NSTAGE) - 1);  // tile 0 and the older Q loads have landed
+    for (int t = 1; t < min(n, P0); ++t) copy_tile(t);
+    wait_ahead(min(n, P0) - 1);
     // Tie the Q registers to the wait: nothing below may read them earlier.
     // (The compiler still could copy them between the load and here; the CPU
     // test tests/test_q_load_isa.py checks the generated code for that.)
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      u32x4 r = __builtin_bit_cast(u32x4, qf[c]);
-      asm volatile("" : "+v"(r));
-      if (!row_ok) r = u32x4{0u, 0u, 0u, 0u};
-      qf[c] = __builtin_bit_cast(bf16x8, r);
-    }
+    for (int X = 0; X < QB; ++X)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        u32x4 r = __builtin_bit_cast(u32x4, qf[X][c]);
+        asm volatile("" : "+v"(r));
+        if (!okq[X]) r = u32x4{0u, 0u, 0u, 0u};
+        qf[X][c] = __builtin_bit_cast(bf16x8, r);
+      }
     tile_barrier();
-    if (computes) load_k(lds);
+    // Scores of tile t, straight from its K tile in LDS (prologue and the
+    // rare recomputation of the max-raise path).
+    auto scores_of = [&](f32x16* Sc, int t) __attribute__((always_inline)) {
+      const unsigned kb = __builtin_amdgcn_readfirstlane((unsigned)((t % NS) * STAGE * 2));
+      bf16x8 kr[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kr[c] = lds_read_k(kb, kaddr[c]);
+      wait_lgkm<0>();
+#pragma unroll
+      for (int c = 0; c < KC; ++c) lds_tie(kr[c]);
+#pragma unroll
+      for (int X = 0; X < QB; ++X) {
+        Sc[X] = mfma_s_first(kr[0], qf[X][0]);
+#pragma unroll
+        for (int c = 1; c < KC; ++c) mfma_s_acc(Sc[X], kr[c], qf[X][c]);
+      }
+      mask_scores(Sc, t);
+    };
+#pragma unroll
+    for (int X = 0; X < QB; ++X)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) q_tie(qf[X][c]);
+    scores_of(S, 0);
+    // The stored max starts at tile 0's exact row max (so the first tile needs
+    // no rescaling pass); rows that see nothing in tile 0 keep -inf.
+#pragma unroll
+    for (int X = 0; X < QB; ++X) {
+      float mx = S[X][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[X][v]);
+      m[X] = half_max(mx) * a.scale_log2;
+    }
 
-    for (int t = 0; t < ntiles; ++t) {
-      const unsigned short* Ks = lds + (t % NSTAGE) * STAGE;
-      const int ti = tile0 + t;
-      const bool tree = ti >= n_prefix;
-      const int nvalid = tree ? a.T : min(NK, L - ti * NK);
+    // Tiles before jm are full prefix tiles (no mask). Tiles 0 .. issued-1
+    // have been queued; at tile j a tile t may be queued once the stage it
+    // takes (t % NS) is free everywhere, i.e. t <= j - 2 + NS. In the steady
+    // state exactly that tile is queued and NS - 4 tiles stay in flight
+    // beyond tile j+1.
+    // Tiles before jm are full prefix tiles (no mask). Tiles 0 .. issued-1
+    // have been queued; at tile j a tile t may be queued once the stage it
+    // takes (t % NS) is free everywhere, i.e. t <= j - 2 + NS. In the steady
+    // state exactly that tile is queued (a full prefix tile, its copies
+    // spread over the slots) and NS - 4 tiles stay in flight beyond tile j+1;
+    // the steady iterations run as their own loop with no other bookkeeping.
+    const int jm = min(n, max(0, L / NK - tile0));
+    int issued = min(n, P0);
+    int st_i = issued;  // stage of tile `issued` (P0 < NS)
+    const unsigned short* kq = kp + (size_t)(tile0 + issued) * NK * D;  // rows of tile `issued`
+    const unsigned short* vq = vp + (size_t)(tile0 + issued) * NK * D;
+    // Stages of tiles j and j+1.
+    int st_c = 0, st_n = 1 % NS;
+    auto step = [&](auto steady_c, int j) __attribute__((always_inline)) {
+      constexpr bool STEADY = decltype(steady_c)::value;
+      // Tile j+1 has landed for every wave and every wave is done with the
+      // stage of tile j-2 (its V registers were consumed during tile j-1).
+      // The V reads of tile j-1 (issued during tile j-1) are waited for one
+      // fragment at a time in the slots.
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (!computes || st * 32 >= nvalid) break;
-        // S^T = K . Q^T for 32 tokens (K fragments already in registers).
-        f32x16 S;
+      for (int X = 0; X < QB; ++X)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) S[v] = 0.f;
+        for (int db = 0; db < DB; ++db) o_tie(O[X][db]);
+      unsigned sb_copy = 0;
+      if constexpr (STEADY) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<((NS - 4) * CPW < 63 ? (NS - 4) * CPW : 63)>());
+        tile_barrier();
+        sb_copy = wlds + (unsigned)(st_i * STAGE * 2);
+      } else if (issued == j - 2 + NS && issued < jm) {
+        // steady state: tile j-2+NS, a full prefix tile, into the freed stage
+        __builtin_amdgcn_s_waitcnt(vmcnt_only<((NS - 4) * CPW < 63 ? (NS - 4) * CPW : 63)>());
+        tile_barrier();
+        copy_full(kq, vq, wlds + (unsigned)(st_i * STAGE * 2));
+        ++issued;
+        st_i = st_i + 1 == NS ? 0 : st_i + 1;
+      } else {
+        const int frontier = j - 2 + NS;
+        wait_ahead(issued - j - 2);
+        tile_barrier();
 #pragma unroll
-        for (int c = 0; c < KC; ++c) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], S, 0, 0, 0);
-        // V^T fragments of this sub-tile: tokens 16kc + 8hh + 0..7, dims 32db + lane%32.
-        bf16x8 va[2][DB];
-        {
-          const unsigned short* vb = Ks + voff + 8 * st * DG * 64;
+        for (int r = 0; r < 2; ++r)
+          if (issued < n && issued <= frontier) {
+            copy_tile(issued);
+            ++issued;
+            st_i = st_i + 1 == NS ? 0 : st_i + 1;
+          }
+      }
+
+      const unsigned kn = __builtin_amdgcn_readfirstlane((unsigned)(st_n * STAGE * 2));  // K tile j+1
+      const unsigned vc = lds_base + voff_b + __builtin_amdgcn_readfirstlane((unsigned)(st_c * STAGE * 2));
+      float nm[QB];
 #pragma unroll
-          for (int kc = 0; kc < 2; ++kc)
+      for (int X = 0; X < QB; ++X) nm[X] = m[X] == -__builtin_inff() ? 0.f : -m[X];
+      float xs[16 * QB], pr[16 * QB], ps[QB][4];
+      bf16x8 Pn[QB][2], kf[KC];
+      f32x16 Sn[QB];
+      i16x4 vh[2][2][DB];  // V^T fragment halves of tile j: [low/high][kc][db]
+      auto fma_p = [&](int p) __attribute__((always_inline)) {
+        xs[p] = fmaf(S[p >> 4][p & 15], a.scale_log2, nm[p >> 4]);
+      };
+      unsigned pk[QB][2][4];  // bf16 pairs of this tile's probabilities
+      auto sum_p = [&](int p) __attribute__((always_inline)) {
+        if ((p & 15) < 4)
+          ps[p >> 4][p & 3] = pr[p];
+        else
+          ps[p >> 4][p & 3] += pr[p];
+        if (p & 1) pk[p >> 4][(p >> 3) & 1][(p & 7) >> 1] = cvt_pk_bf16(pr[p - 1], pr[p]);
+      };
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const i16x4 lo = lds_read_tr(vb + (4 * kc * DG + 2 * db) * 64);
-              const i16x4 hi = lds_read_tr(vb + ((4 * kc + 1) * DG + 2 * db) * 64);
-              va[kc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int e = 0; e < EPS; ++e) fma_p(e);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NSLOT>([&](auto kk) __attribute__((always_inline)) {
+        constexpr int k = decltype(kk)::value;
+        if constexpr (k < NPV) {
+          // P.V of tile j-1 (zeros before the first tile)
+          constexpr int f = k / QB, X = k % QB, kc = f / DB, db = f % DB;
+          if constexpr (X == 0) wait_lgkm<Sch::vwait(f)>();
+          mfma_pv(O[X][db], vf[kc][db], P[X][kc]);
+          // This slot's exp waits for the MFMA issue (the compiler would put
+          // the quarter-rate exp first and hold the MFMA up behind it).
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) asm volatile("" : "+v"(xs[k * EPS + e]));
+        } else {
+          // scores of tile j+1 (computed on stale data past the piece's last tile, then unused)
+          constexpr int c = (k - NPV) / QB, X = (k - NPV) % QB;
+          if constexpr (X == 0) {
+            wait_lgkm<Sch::kwait(c)>();
+            lds_tie(kf[c]);
+          }
+          if constexpr (c == 0)
+            Sn[X] = mfma_s_first(kf[c], qf[X][c]);
+          else
+            mfma_s_acc(Sn[X], kf[c], qf[X][c]);
+        }
+        // V^T fragments of tile j into the registers the P.V above has freed.
+        static_for<0, 2 * DB>([&](auto ff) __attribute__((always_inline)) {
+          constexpr int f = decltype(ff)::value, kc = f / DB, db = f % DB;
+          static_for<0, 2>([&](auto hh_) __attribute__((always_inline)) {
+            constexpr int h = decltype(hh_)::value;
+            if constexpr (Sch::vslot(f, h) == k)
+              vh[h][kc][db] = lds_read_v<((4 * kc + h) * DG + 2 * db) * 128>(vc);
+          });
+        });
+        // Steady state: this wave's copies of the refilled tile, spread over the slots.
+        if constexpr (STEADY) {
+          static_for<0, CPW>([&](auto ii) __attribute__((always_inline)) {
+            constexpr int i = decltype(ii)::value;
+            if constexpr (1 + i * (NSLOT / CPW) == k) {
+              if constexpr (i < KPW)
+                copy16_to_lds_at<i * NWAVE * RPB * D * 2>(kq, kofs[i], sb_copy);
+              else
+                copy16_to_lds_at<(TILE + (i - KPW) * NWAVE * RPB * D) * 2>(vq, vofs[i - KPW], sb_copy);
             }
+          });
         }
-        // S[v] scores token st*32 + 16*(v/8) + 8*hh + v%8 of the tile. On the
-        // tree tile and on a ragged last tile, bit v of `vis` says whether that
-        // token is seen; hidden scores get -inf added (no compares, no masks).
-        if (tree || st * 32 + 32 > nvalid) {
-          unsigned vis;
-          const int j0 = st * 32 + 8 * hh;
-          if (tree) {
-            vis = (unsigned)((anc_row >> j0) & 0xffull) | ((unsigned)((anc_row >> (j0 + 16)) & 0xffull) << 8);
-          } else {
-            const int n0 = min(max(nvalid - j0, 0), 8), n1 = min(max(nvalid - j0 - 16, 0), 8);
-            vis = ((1u << n0) - 1u) | (((1u << n1) - 1u) << 8);
-          }
+        // K fragments of tile j+1
+        static_for<0, KC>([&](auto cc) __attribute__((always_inline)) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (Sch::kslot(c) == k) kf[c] = lds_read_k(kn, kaddr[c]);
+        });
 #pragma unroll
-          for (int v = 0; v < 16; ++v) S[v] += __uint_as_float((((vis >> v) & 1u) - 1u) & 0xff800000u);
+        for (int e = 0; e < EPS; ++e) {
+          if (k + 1 < NSLOT) fma_p((k + 1) * EPS + e);
+          pr[k * EPS + e] = fast_exp2(xs[k * EPS + e]);
+          if (k >= 1) sum_p((k - 1) * EPS + e);
         }
-        // Probabilities against the stored max m; the row sum adds them in fp32
-        // (four partial sums), the P.V product takes them rounded to bf16. The
-        // sum bounds every term, so if it stays <= 256 so does each
-        // p = 2^(s - m) and m can stay. Otherwise (and always while m is still
-        // -inf) take the exact row max over both half-rows; if it exceeds m by
-        // more than 8, raise m, rescale l and O, and recompute.
-        float pr[16];
-        auto probs = [&]() __attribute__((always_inline)) {
-          const float nm = m == -__builtin_inff() ? 0.f : -m;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) pr[v] = fast_exp2(fmaf(S[v], a.scale_log2, nm));
-        };
-        auto row_sum = [&]() __attribute__((always_inline)) {
-          const float s0 = (pr[0] + pr[4]) + (pr[8] + pr[12]), s1 = (pr[1] + pr[5]) + (pr[9] + pr[13]);
-          const float s2 = (pr[2] + pr[6]) + (pr[10] + pr[14]), s3 = (pr[3] + pr[7]) + (pr[11] + pr[15]);
-          return (s0 + s1) + (s2 + s3);
-        };
-        probs();
-        float ls = row_sum();
-        if (__any(!(ls <= 256.0f) || m == -__builtin_inff())) {
-          float mx0 = fmaxf(fmaxf(S[0], S[1]), S[2]), mx1 = fmaxf(fmaxf(S[3], S[4]), S[5]);
-          float mx2 = fmaxf(fmaxf(S[6], S[7]), S[8]), mx3 = fmaxf(fmaxf(S[9], S[10]), S[11]);
-          float mx4 = fmaxf(fmaxf(S[12], S[13]), S[14]);
-          float mx = fmaxf(fmaxf(fmaxf(mx0, mx1), fmaxf(mx2, mx3)), fmaxf(mx4, S[15]));
-          mx = half_max(mx) * a.scale_log2;
-          if (__any(mx > m + 8.0f)) {
-            const float mn = fmaxf(m, mx);
-            const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mn);
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) O[db] *= alpha;
-            probs();
-            ls = row_sum();
-          }
+        if constexpr (k >= NPV) {
+          // the score MFMA first in the slot, the VALU work after it
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x602, 16, 0);  // VALU and transcendental
         }
-        bf16x8 P[2];
+        __builtin_amdgcn_sched_barrier(0);
+      });
 #pragma unroll
-        for (int v = 0; v < 16; ++v) P[v >> 3][v & 7] = (__bf16)pr[v];
-        l += ls;
-        // K fragments of the next sub-tile of this tile, read while P.V runs.
-        if (st == 0 && nvalid > 32) load_k(Ks + 32 * D);
-        // O^T += V^T . P^T over the two 16-token k-chunks of this sub-tile.
+      for (int e = 0; e < EPS; ++e) sum_p((NSLOT - 1) * EPS + e);
+#pragma unroll
+      for (int X = 0; X < QB; ++X)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kc][db], P[kc], O[db], 0, 0, 0);
-      }
-      if (t + 1 < ntiles) {
-        // Tile t+1 has landed for every wave (at most tiles t+2, t+3 still in
-        // flight: tiles up to t+3 have been queued) and every wave's reads of
-        // tile t are done: its stage takes tile t+4. Then the K fragments of
-        // tile t+1.
-        __builtin_amdgcn_s_waitcnt(kLgkmZero);
-        wait_tiles(min(ntiles - 2 - t, 2));
-        tile_barrier();
-        if (t + NSTAGE < ntiles) copy_tile(t + NSTAGE);
-        if (computes) load_k(lds + ((t + 1) % NSTAGE) * STAGE);
-      }
-    }
-    __syncthreads();  // no wave reads the tile buffers any more (all copies landed before the last barrier)
+          Pn[X][kc] = __builtin_bit_cast(bf16x8, u32x4{pk[X][kc][0], pk[X][kc][1], pk[X][kc][2], pk[X][kc][3]});
 
-    // Epilogue: O^T holds dims db*32 + 8*(v/4) + 4*hh + v%4 of query row `row`.
-    // Normalise, round to bf16 and stage this wave's 32 rows in LDS (rows
-    // padded by 16 bytes), then write them out as whole contiguous rows.
-    const float lt = half_sum(l);
-    const float inv = 1.0f / lt;
-    unsigned short* stg = lds + wave * 32 * SROW;
-    if (computes) {
+      float ls[QB];
+      bool need = false;
+#pragma unroll
+      for (int X = 0; X < QB; ++X) {
+        ls[X] = (ps[X][0] + ps[X][1]) + (ps[X][2] + ps[X][3]);
+        need |= !(ls[X] <= 256.0f) || m[X] == -__builtin_inff();
+      }
+      // The sum bounds every term: while it stays <= 256 the stored max can
+      // stay. Otherwise (and while m is -inf) take the exact row max over both
+      // half-rows; if it exceeds m by more than 8, raise m, rescale l and O,
+      // and recompute the tile's probabilities. The scores of tile j are
+      // recomputed from its K tile, still in LDS (its stage is refilled two
+      // tiles later).
+      if (__any(need)) {
+        f32x16 Sj[QB];
+        wait_lgkm<0>();
+        scores_of(Sj, j);
+#pragma unroll
+        for (int X = 0; X < QB; ++X) {
+          float mx = Sj[X][0];
+#pragma unroll
+          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, Sj[X][v]);
+          mx = half_max(mx) * a.scale_log2;
+          if (__any(mx > m[X] + 8.0f)) {
+            const float mn = fmaxf(m[X], mx);
+            const float alpha = m[X] == -__builtin_inff() ? 0.f : fast_exp2(m[X] - mn);
+            m[X] = mn;
+            l[X] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              o_fence(O[X][db]);
+              O[X][db] *= alpha;
+              o_fence(O[X][db]);
+            }
+            const float nmx = mn == -__builtin_inff() ? 0.f : -mn;
+            float q4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float p = fast_exp2(fmaf(Sj[X][v], a.scale_log2, nmx));
+              q4[v & 3] += p;
+              Pn[X][v >> 3][v & 7] = (__bf16)p;
+            }
+            ls[X] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int X = 0; X < QB; ++X) {
+        l[X] += ls[X];
+        S[X] = Sn[X];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) P[X][kc] = Pn[X][kc];
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          vf[kc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vh[0][kc][db], vh[1][kc][db], 0, 1, 2, 3, 4,
+                                                                           5, 6, 7));
+      // Masks of tile j+1 (known now that its scores are; never needed in the steady state).
+      if constexpr (!STEADY)
+        if (j + 1 >= jm && j + 1 < n) mask_scores(S, j + 1);
+      st_c = st_n;
+      st_n = st_n + 1 == NS ? 0 : st_n + 1;
+      kq = kp + (size_t)(tile0 + issued) * NK * D;
+      vq = vp + (size_t)(tile0 + issued) * NK * D;
+    };
+    for (int j = 0; j < n;) {
+      step(std::false_type{}, j);
+      ++j;
+    }
+    // P.V of the last tile.
+    wait_lgkm<0>();
+#pragma unroll
+    for (int f = 0; f < 2 * DB; ++f)
+#pragma unroll
+      for (int X = 0; X < QB; ++X) mfma_pv_after_valu(O[X][f % DB], vf[f / DB][f % DB], P[X][f / DB]);
+#pragma unroll
+    for (int X = 0; X < QB; ++X)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o_fence(O[X][db]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+    __syncthreads();  // every copy has landed and no wave reads the tile buffers any more
+
+    // Epilogue: O^T holds dims db*32 + 8*(v/4) + 4*hh + v%4 of row rowq[X].
+    // Normalise, round to bf16 and stage this wave's rows in LDS (rows padded
+    // by 16 bytes), then write them out as whole contiguous rows.
+    unsigned short* stg = lds + wave * 32 * QB * SROW;
+#pragma unroll
+    for (int X = 0; X < QB; ++X) {
+      const float lt = half_sum(l[X]);
+      const float inv = 1.0f / lt;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + 8 * g4 + 4 * hh;
           u32x2 pk;
-          pk[0] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 0] * inv) |
-                  ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 1] * inv) << 16);
-          pk[1] = (unsigned)float_to_bf16_bits(O[db][4 * g4 + 2] * inv) |
-                  ((unsigned)float_to_bf16_bits(O[db][4 * g4 + 3] * inv) << 16);
-          *(u32x2*)(stg + l32 * SROW + d) = pk;
+          pk[0] = (unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 0] * inv) |
+                  ((unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 1] * inv) << 16);
+          pk[1] = (unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 2] * inv) |
+                  ((unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 3] * inv) << 16);
+          *(u32x2*)(stg + (32 * X + l32) * SROW + d) = pk;
         }
+      if (okq[X] && hh == 0) a.slot_lse2[(size_t)slot * a.M + rowq[X]] = m[X] + fast_log2(lt);
     }
-    if (row_ok && hh == 0) a.slot_lse2[(size_t)slot * a.M + row] = m + fast_log2(lt);
     __syncthreads();
-    const int wrow0 = blockIdx.y * a.rows_per_group + wave * 32;  // first row of this wave
 #pragma unroll
-    for (int i = 0; i < (computes ? 32 * DCH / 64 : 0); ++i) {
+    for (int i = 0; i < 32 * QB * DCH / 64; ++i) {
       const int u = i * 64 + lane;
       const int rr = u / DCH, c = u % DCH;
       const u32x4 val = *(const u32x4*)(stg + rr * SROW + c * 8);
       if (wrow0 + rr < row_limit) *(u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8) = val;
     }
-    if (has_tree && g == 0 && blockIdx.y == 0 && tid == 0) {
+    // The workgroup holding the first tree tile of (b, KV head 0) reports the tree check.
+    if (has_tree && tile0 <= n_prefix && g == 0 && blockIdx.y == 0 && tid == 0) {
       a.err_b[b] = bad_s;
       if (bad_s) atomicOr(a.status, kStatusBadTree);
     }
@@ -391,44 +698,49 @@ __global__ void __launch_bounds__(threads_for<WQ>()) prefix_mfma_kernel(PrefixAr
   }
 }
 
-template <int D>
-KernelFn pick_d(int wq) {
-  switch (wq) {
-    case 1: return prefix_mfma_kernel<D, 1>;
-    case 2: return prefix_mfma_kernel<D, 2>;
-    case 3: return prefix_mfma_kernel<D, 3>;
-    case 4: return prefix_mfma_kernel<D, 4>;
-    case 5: return prefix_mfma_kernel<D, 5>;
-    case 6: return prefix_mfma_kernel<D, 6>;
-    case 7: return prefix_mfma_kernel<D, 7>;
-    case 8: return prefix_mfma_kernel<D, 8>;
-    default: return nullptr;
-  }
-}
+typedef void (*KernelFn)(PrefixArgs);
 
-KernelFn pick(int D, int waves, int qb) {
-  if (qb == 2) return prefix_mfma2_pick(D, waves);
-  if (qb != 1) return nullptr;
-  return D == 128 ? pick_d<128>(waves) : D == 64 ? pick_d<64>(waves) : nullptr;
-}
+// Instances: every (QB, waves) the plan can pick -- QB = 2 with 1, 2 or 4
+// waves, QB = 1 (on request, or for a single 32-row block) with 1, 2 or 4 --
+// at D = 128 and 64, each with the stage count that fills the LDS.
+struct Inst {
+  int D, qb, waves, stages;
+  KernelFn fn;
+};
+constexpr int kNsLarge = 9;  // 144 KB of 16 KB stages (D = 128)
+const Inst kInst[] = {
+    {128, 2, 4, kNsLarge, prefix_mfma_kernel<128, 2, 4, kNsLarge>},
+    {128, 2, 2, kNsLarge, prefix_mfma_kernel<128, 2, 2, kNsLarge>},
+    {128, 2, 1, kNsLarge, prefix_mfma_kernel<128, 2, 1, kNsLarge>},
+    {128, 1, 4, kNsLarge, prefix_mfma_kernel<128, 1, 4, kNsLarge>},
+    {128, 1, 2, kNsLarge, prefix_mfma_kernel<128, 1, 2, kNsLarge>},
+    {128, 1, 1, kNsLarge, prefix_mfma_kernel<128, 1, 1, kNsLarge>},
+    {64, 2, 4, 10, prefix_mfma_kernel<64, 2, 4, 10>},
+    {64, 2, 2, 10, prefix_mfma_kernel<64, 2, 2, 10>},
+    {64, 2, 1, 10, prefix_mfma_kernel<64, 2, 1, 10>},
+    {64, 1, 4, 10, prefix_mfma_kernel<64, 1, 4, 10>},
+    {64, 1, 2, 10, prefix_mfma_kernel<64, 1, 2, 10>},
+    {64, 1, 1, 10, prefix_mfma_kernel<64, 1, 1, 10>},
+};
 
-int threads_of(int waves, int qb) { return qb == 2 || waves <= 4 ? 256 : 512; }
+const Inst* find(int D, int qb, int waves) {
+  for (const Inst& i : kInst)
+    if (i.D == D && i.qb == qb && i.waves == waves) return &i;
+  return nullptr;
+}
 
 }  // namespace
 }  // namespace mfma
 
-using mfma::KernelFn;
 using mfma::PrefixArgs;
-using mfma::pick;
-using mfma::threads_of;
 
-bool prefix_mfma_supported(int D, int waves, int qb) { return pick(D, waves, qb) != nullptr; }
+bool prefix_mfma_supported(int D, int waves, int qb) { return mfma::find(D, qb, waves) != nullptr; }
 
 int prefix_mfma_occupancy(int D, int waves, int qb) {
-  KernelFn k = pick(D, waves, qb);
-  if (!k) return 0;
+  const mfma::Inst* in = mfma::find(D, qb, waves);
+  if (!in) return 0;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), threads_of(waves, qb), 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(in->fn), waves * 64, 0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;
@@ -436,8 +748,8 @@ int prefix_mfma_occupancy(int D, int waves, int qb) {
 
 hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                               int* err_b, int* status, hipStream_t s) {
-  KernelFn k = pick(d.D, pl.waves, pl.qb);
-  if (!k) return hipErrorInvalidValue;
+  const mfma::Inst* inst = mfma::find(d.D, pl.qb, pl.waves);
+  if (!inst) return hipErrorInvalidValue;
   PrefixArgs a;
   a.q = static_cast<const unsigned short*>(in.q);
   a.k = static_cast<const unsigned short*>(in.k_cache);
@@ -459,9 +771,9 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
   a.M = d.M;
   a.nwg = pl.nwg;
   a.rows_per_group = pl.rows_per_group;
-  a.tree_tiles = in.k_tree ? 1 : 0;
+  a.tree_tiles = in.k_tree ? tree_tiles_for(d.T, mfma::NK) : 0;
   a.scale_log2 = d.scale_log2;
-  hipLaunchKernelGGL(k, dim3(pl.nwg, pl.row_groups), dim3(threads_of(pl.waves, pl.qb)), 0, s, a);
+  hipLaunchKernelGGL(inst->fn, dim3(pl.nwg, pl.row_groups), dim3(pl.waves * 64), 0, s, a);
   return hipGetLastError();
 }
 

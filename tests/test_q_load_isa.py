@@ -23,7 +23,7 @@ import pytest
 from speculative_decoding_verification_hybrid_amd import _build
 
 VMEM = re.compile(r"^\s*(global_|buffer_|flat_|scratch_)(load|store|atomic)")
-KERNEL = re.compile(r"^(_ZN3hta4mfma12_GLOBAL__N_11[89]prefix_mfma2?_kernelILi(\d+)ELi(\d+)E\S*):", re.M)
+KERNEL = re.compile(r"^(_ZN3hta4mfma12_GLOBAL__N_118prefix_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E\S*):", re.M)
 
 
 def _regs(line):
@@ -77,7 +77,7 @@ def check_kernel(body):
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-@pytest.mark.parametrize("src,instances", [("prefix_mfma.hip", 16), ("prefix_mfma2.hip", 8)])
+@pytest.mark.parametrize("src,instances", [("prefix_mfma.hip", 12)])
 def test_q_fragment_loads_untouched_until_waited(tmp_path, src, instances):
     out = tmp_path / (src + ".s")
     cmd = [_build.hipcc()] + _build.flags_for(src) + ["--cuda-device-only", "-S", os.path.join(_build.CSRC, src),
@@ -86,13 +86,13 @@ def test_q_fragment_loads_untouched_until_waited(tmp_path, src, instances):
     assert r.returncode == 0, r.stderr[-2000:]
     s = out.read_text()
     kernels = list(KERNEL.finditer(s))
-    assert len(kernels) == instances  # every (D, waves) instance
+    assert len(kernels) == instances  # every (D, QB, waves, stages) instance
     for m in kernels:
         end = s.index("s_endpgm", m.end())
         body = [l for l in s[m.end():end].split("\n") if l.strip() and not l.strip().startswith(";")
                 and not l.strip().startswith(".")]
         n, bad = check_kernel(body)
-        assert n > 0 and not bad, f"D={m.group(2)} WQ={m.group(3)}: {bad[:3]}"
+        assert n > 0 and not bad, f"D={m.group(2)} QB={m.group(3)} waves={m.group(4)}: {bad[:3]}"
 
 
 def test_checker_catches_early_use():
