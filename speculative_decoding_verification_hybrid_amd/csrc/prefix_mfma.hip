@@ -68,63 +68,24 @@ namespace mfma {
 namespace {
 
 // Static schedule of one tile's slots (see the header comment): slot k
-// issues one MFMA (P.V for k < NPV, then scores), then its LDS reads. The
-// reads are spread so that no slot asks the LDS for much more than the MFMA
-// takes: the KC K fragments of the next tile evenly over the P.V slots (a
-// score MFMA reads its fragment at least NPV/2 slots later), the 4*DB halves
-// of V^T fragments of this tile evenly over the score slots (after the last
-// P.V MFMA of the old fragment, at least NSC/2 slots before the next tile's
-// first use). kwait(c) is the lgkmcnt that covers K fragment c at its first
-// score MFMA.
+// issues one MFMA (P.V for k < NPV, then scores), then its LDS reads. The KC
+// K fragments of the next tile are read over the P.V slots from slot TOP on
+// (the barrier that publishes the tile comes right before slot TOP) up to
+// four slots before the first score MFMA, where they are waited for once. The 4*DB halves of V^T fragments of this tile are
+// read over the score slots but the last two (their registers are free once
+// the P.V MFMAs are done) and waited for once, at the top of the next tile.
 template <int D, int QB>
 struct SlotSchedule {
   static constexpr int KC = D / 16, DB = D / 32, NPV = 2 * DB * QB, NSC = KC * QB, NSLOT = NPV + NSC;
-  static constexpr int kslot(int c) { return c * NPV / KC; }
-  static constexpr int vslot(int f, int h) { return NPV + (2 * f + h) * NSC / (4 * DB); }
-  static constexpr int nv_in(int s) {
-    int n = 0;
-    for (int f = 0; f < 2 * DB; ++f)
-      for (int h = 0; h < 2; ++h) n += vslot(f, h) == s;
-    return n;
-  }
-  static constexpr int nk_in(int s) {
-    int n = 0;
-    for (int c = 0; c < KC; ++c) n += kslot(c) == s;
-    return n;
-  }
-  static constexpr int ops_before(int s) {
-    int n = 0;
-    for (int t = 0; t < s; ++t) n += nv_in(t) + nk_in(t);
-    return n;
-  }
-  // index of K read c in issue order (a slot issues its V reads, then its K
-  // reads in order of c)
-  static constexpr int kidx(int c) {
-    int n = ops_before(kslot(c)) + nv_in(kslot(c));
-    for (int e = 0; e < c; ++e) n += kslot(e) == kslot(c);
-    return n;
-  }
-  static constexpr int kwait(int c) { return ops_before(NPV + c * QB) - kidx(c) - 1; }
-  // index of the read of half h of V fragment f in issue order (the V reads
-  // of a slot in order of (f, h))
-  static constexpr int vidx(int f, int h) {
-    int n = ops_before(vslot(f, h));
-    for (int g = 0; g < 2 * DB; ++g)
-      for (int e = 0; e < 2; ++e)
-        if ((g < f || (g == f && e < h)) && vslot(g, e) == vslot(f, h)) ++n;
-    return n;
-  }
-  // lgkmcnt that covers V fragment f (read during the previous tile) at its
-  // first P.V MFMA, slot f*QB: the reads issued after it in the previous tile
-  // plus this tile's reads before that slot.
-  static constexpr int vwait(int f) { return ops_before(NSLOT) - vidx(f, 1) - 1 + ops_before(f * QB); }
+  static constexpr int TOP = NPV >= 8 ? 2 : 1;
+  static constexpr int kslot(int c) { return TOP + c * (NPV - TOP - 4 > 0 ? NPV - TOP - 4 : 1) / KC; }
+  static constexpr int vslot(int f, int h) { return NPV + (2 * f + h) * (NSC - 2) / (4 * DB); }
   static constexpr bool valid() {
     for (int f = 0; f < 2 * DB; ++f)
-      if (vslot(f, 1) >= NSLOT || vslot(f, 0) < (f + 1) * QB) return false;
+      for (int h = 0; h < 2; ++h)
+        if (vslot(f, h) < NPV || vslot(f, h) >= NSLOT) return false;
     for (int c = 0; c < KC; ++c)
-      if (kslot(c) >= NPV + c * QB || kwait(c) < 0) return false;
-    for (int f = 0; f < 2 * DB; ++f)
-      if (vwait(f) < 0) return false;
+      if (kslot(c) < TOP || kslot(c) >= NPV) return false;
     return true;
   }
   static_assert(valid(), "slot schedule");
@@ -352,6 +313,24 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[kc][db][e] = (__bf16)0.f;
+    // The first tile's P.V operands are these zeros: hide their value from the
+    // compiler, so it does not materialise them right before the (inline
+    // assembly) MFMAs, whose operand hazards it cannot see.
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int X = 0; X < QB; ++X) {
+        u32x4 r = __builtin_bit_cast(u32x4, P[X][kc]);
+        asm volatile("" : "+v"(r));
+        P[X][kc] = __builtin_bit_cast(bf16x8, r);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x4 r = __builtin_bit_cast(u32x4, vf[kc][db]);
+        asm volatile("" : "+v"(r));
+        vf[kc][db] = __builtin_bit_cast(bf16x8, r);
+      }
+    }
 
     // Prologue: queue tile 0, the Q loads and tile 1 only, wait for tile 0
     // and Q, score tile 0. Every CU asking for all its stages at once (every
@@ -392,10 +371,10 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
         qf[X][c] = __builtin_bit_cast(bf16x8, r);
       }
     tile_barrier();
-    // Scores of tile t, straight from its K tile in LDS (prologue and the
-    // rare recomputation of the max-raise path).
-    auto scores_of = [&](f32x16* Sc, int t) __attribute__((always_inline)) {
-      const unsigned kb = __builtin_amdgcn_readfirstlane((unsigned)((t % NS) * STAGE * 2));
+    // Scores of the tile in the stage at LDS byte offset kb, straight from its
+    // K tile in LDS (prologue and the rare recomputation of the max-raise path);
+    // t is the tile's index in the piece, for its mask.
+    auto scores_of = [&](f32x16* Sc, unsigned kb, int t) __attribute__((always_inline)) {
       bf16x8 kr[KC];
 #pragma unroll
       for (int c = 0; c < KC; ++c) kr[c] = lds_read_k(kb, kaddr[c]);
@@ -414,100 +393,165 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     for (int X = 0; X < QB; ++X)
 #pragma unroll
       for (int c = 0; c < KC; ++c) q_tie(qf[X][c]);
-    scores_of(S, 0);
+    scores_of(S, 0u, 0);
     // The stored max starts at tile 0's exact row max (so the first tile needs
-    // no rescaling pass); rows that see nothing in tile 0 keep -inf.
+    // no rescaling pass); rows that see nothing in tile 0 keep -inf. The
+    // softmax adds nm = -m (0 while m is -inf); lim bounds a tile's
+    // probability sum below which m may stay (-1 while m is -inf, so that the
+    // first visible score takes the exact path).
+    float nm[QB], lim[QB];
 #pragma unroll
     for (int X = 0; X < QB; ++X) {
       float mx = S[X][0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[X][v]);
       m[X] = half_max(mx) * a.scale_log2;
+      nm[X] = m[X] == -__builtin_inff() ? 0.f : -m[X];
+      lim[X] = m[X] == -__builtin_inff() ? -1.f : 256.f;
     }
 
     // Tiles before jm are full prefix tiles (no mask). Tiles 0 .. issued-1
     // have been queued; at tile j a tile t may be queued once the stage it
     // takes (t % NS) is free everywhere, i.e. t <= j - 2 + NS. In the steady
-    // state exactly that tile is queued and NS - 4 tiles stay in flight
-    // beyond tile j+1.
-    // Tiles before jm are full prefix tiles (no mask). Tiles 0 .. issued-1
-    // have been queued; at tile j a tile t may be queued once the stage it
-    // takes (t % NS) is free everywhere, i.e. t <= j - 2 + NS. In the steady
-    // state exactly that tile is queued (a full prefix tile, its copies
-    // spread over the slots) and NS - 4 tiles stay in flight beyond tile j+1;
-    // the steady iterations run as their own loop with no other bookkeeping.
+    // state exactly that tile is queued and NS - 4 tiles stay in flight beyond
+    // tile j+1; past the piece's last tile nothing is.
     const int jm = min(n, max(0, L / NK - tile0));
     int issued = min(n, P0);
-    int st_i = issued;  // stage of tile `issued` (P0 < NS)
     const unsigned short* kq = kp + (size_t)(tile0 + issued) * NK * D;  // rows of tile `issued`
     const unsigned short* vq = vp + (size_t)(tile0 + issued) * NK * D;
-    // Stages of tiles j and j+1.
-    int st_c = 0, st_n = 1 % NS;
-    auto step = [&](auto steady_c, int j) __attribute__((always_inline)) {
-      constexpr bool STEADY = decltype(steady_c)::value;
-      // Tile j+1 has landed for every wave and every wave is done with the
-      // stage of tile j-2 (its V registers were consumed during tile j-1).
-      // The V reads of tile j-1 (issued during tile j-1) are waited for one
-      // fragment at a time in the slots.
+    constexpr unsigned SB = STAGE * 2;  // bytes per stage
+    auto rot = [](unsigned o) __attribute__((always_inline)) { return o + SB == NS * SB ? 0u : o + SB; };
+    unsigned op = 0u, oc = 0u, on = rot(0u);  // stage byte offsets of tiles j-1, j and j+1
+    unsigned ocp = (unsigned)((NS - 2) % NS) * SB;  // stage byte offset of tile j-2+NS
+    // Probability sum of tile j-1, checked (and added to l) at the start of tile j.
+    float lsp[QB];
+#pragma unroll
+    for (int X = 0; X < QB; ++X) lsp[X] = 0.f;
+
+    // The lazy-max check of tile t's probabilities Pt (sum lst), before their
+    // P.V: the sum bounds every term, so while it stays <= 256 the stored max
+    // can stay. Otherwise (and while m is -inf) take the exact row max over
+    // both half-rows; if it exceeds m by more than 8, raise m, rescale l and O,
+    // and recompute the tile's probabilities from its scores, recomputed from
+    // its K tile (still in LDS at stage byte offset ot: a stage is refilled
+    // two tiles after its tile). Then the sum joins l.
+    auto check = [&](int t, bf16x8(&Pt)[QB][2], float(&lst)[QB], unsigned ot) __attribute__((always_inline)) {
+      bool need = false;
+#pragma unroll
+      for (int X = 0; X < QB; ++X) need |= !(lst[X] <= lim[X]);
+      if (__any(need)) {
+        f32x16 Sj[QB];
+        wait_lgkm<0>();
+        scores_of(Sj, ot, t);
+#pragma unroll
+        for (int X = 0; X < QB; ++X) {
+          float mx = Sj[X][0];
+#pragma unroll
+          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, Sj[X][v]);
+          mx = half_max(mx) * a.scale_log2;
+          if (__any(mx > m[X] + 8.0f)) {
+            const float mn = fmaxf(m[X], mx);
+            const float alpha = m[X] == -__builtin_inff() ? 0.f : fast_exp2(m[X] - mn);
+            m[X] = mn;
+            nm[X] = mn == -__builtin_inff() ? 0.f : -mn;
+            lim[X] = mn == -__builtin_inff() ? -1.f : 256.f;
+            l[X] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              o_fence(O[X][db]);
+              O[X][db] *= alpha;
+              o_fence(O[X][db]);
+            }
+            float q4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float p = fast_exp2(fmaf(Sj[X][v], a.scale_log2, nm[X]));
+              q4[v & 3] += p;
+              Pt[X][v >> 3][v & 7] = (__bf16)p;
+            }
+            lst[X] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int X = 0; X < QB; ++X) l[X] += lst[X];
+    };
+
+    // Tile j: its scores are in Sc, tile j-1's probabilities in Pc (sum in
+    // lsp); leaves tile j+1's scores in Sn and tile j's probabilities in Pn
+    // (sum in lsp). Two consecutive tiles swap the roles of the two register
+    // sets, so no scores or probabilities are copied between tiles.
+    constexpr int TOP = NPV >= 8 ? 2 : 1;  // P.V slots issued ahead of the barrier
+    auto step = [&](const int j, f32x16(&Sc)[QB], f32x16(&Sn)[QB], bf16x8(&Pc)[QB][2], bf16x8(&Pn)[QB][2])
+                    __attribute__((always_inline)) {
+      if (j > 0) check(j - 1, Pc, lsp, op);
 #pragma unroll
       for (int X = 0; X < QB; ++X)
 #pragma unroll
         for (int db = 0; db < DB; ++db) o_tie(O[X][db]);
-      unsigned sb_copy = 0;
-      if constexpr (STEADY) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<((NS - 4) * CPW < 63 ? (NS - 4) * CPW : 63)>());
-        tile_barrier();
-        sb_copy = wlds + (unsigned)(st_i * STAGE * 2);
-      } else if (issued == j - 2 + NS && issued < jm) {
-        // steady state: tile j-2+NS, a full prefix tile, into the freed stage
-        __builtin_amdgcn_s_waitcnt(vmcnt_only<((NS - 4) * CPW < 63 ? (NS - 4) * CPW : 63)>());
-        tile_barrier();
-        copy_full(kq, vq, wlds + (unsigned)(st_i * STAGE * 2));
-        ++issued;
-        st_i = st_i + 1 == NS ? 0 : st_i + 1;
-      } else {
-        const int frontier = j - 2 + NS;
-        wait_ahead(issued - j - 2);
-        tile_barrier();
+      wait_lgkm<0>();  // this wave's V reads of tile j-1
+      // Top of the tile (after the first TOP P.V MFMAs, which run meanwhile):
+      // tile j+1 has landed for every wave (each waits for its own copies and
+      // the barrier publishes them), and every wave is done with the stage of
+      // tile j-2 (its V registers were consumed during tile j-1): it takes
+      // tile j-2+NS. In the steady state that is a full prefix tile with
+      // NS - 4 tiles in flight beyond tile j+1 (one fixed wait, precomputed
+      // copy offsets); otherwise (the ring filling up, masked copies, the
+      // tail) up to two tiles are queued with the general copy.
+      auto top = [&]() __attribute__((always_inline)) {
+        const int t = j - 2 + NS;
+        if (t < jm && issued == t) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_only<((NS - 4) * CPW < 63 ? (NS - 4) * CPW : 63)>());
+          tile_barrier();
+          copy_full(kq, vq, wlds + ocp);
+          ++issued;
+          kq += NK * D;
+          vq += NK * D;
+        } else {
+          wait_ahead(issued - j - 2);
+          tile_barrier();
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-          if (issued < n && issued <= frontier) {
-            copy_tile(issued);
-            ++issued;
-            st_i = st_i + 1 == NS ? 0 : st_i + 1;
-          }
-      }
-
-      const unsigned kn = __builtin_amdgcn_readfirstlane((unsigned)(st_n * STAGE * 2));  // K tile j+1
-      const unsigned vc = lds_base + voff_b + __builtin_amdgcn_readfirstlane((unsigned)(st_c * STAGE * 2));
-      float nm[QB];
-#pragma unroll
-      for (int X = 0; X < QB; ++X) nm[X] = m[X] == -__builtin_inff() ? 0.f : -m[X];
-      float xs[16 * QB], pr[16 * QB], ps[QB][4];
-      bf16x8 Pn[QB][2], kf[KC];
-      f32x16 Sn[QB];
-      i16x4 vh[2][2][DB];  // V^T fragment halves of tile j: [low/high][kc][db]
-      auto fma_p = [&](int p) __attribute__((always_inline)) {
-        xs[p] = fmaf(S[p >> 4][p & 15], a.scale_log2, nm[p >> 4]);
+          for (int r = 0; r < 2; ++r)
+            if (issued < n && issued <= t) {
+              copy_tile(issued);
+              ++issued;
+            }
+          kq = kp + (size_t)(tile0 + issued) * NK * D;
+          vq = vp + (size_t)(tile0 + issued) * NK * D;
+        }
       };
+
+      const unsigned kn = on;                      // K tile j+1
+      const unsigned vc = lds_base + voff_b + oc;  // V tile j
+      float xs[16 * QB], pr[16 * QB], ps[QB];
+      bf16x8 kf[KC];
+      i16x4 vh[2][2][DB];     // V^T fragment halves of tile j: [low/high][kc][db]
       unsigned pk[QB][2][4];  // bf16 pairs of this tile's probabilities
+      auto fma_p = [&](int p) __attribute__((always_inline)) {
+        xs[p] = fmaf(Sc[p >> 4][p & 15], a.scale_log2, nm[p >> 4]);
+      };
       auto sum_p = [&](int p) __attribute__((always_inline)) {
-        if ((p & 15) < 4)
-          ps[p >> 4][p & 3] = pr[p];
+        if ((p & 15) == 0)
+          ps[p >> 4] = pr[p];
         else
-          ps[p >> 4][p & 3] += pr[p];
+          ps[p >> 4] += pr[p];
         if (p & 1) pk[p >> 4][(p >> 3) & 1][(p & 7) >> 1] = cvt_pk_bf16(pr[p - 1], pr[p]);
       };
+      // The scaled scores run two slots ahead of their exp (a transcendental
+      // reading a VALU result of the previous instruction needs a wait state).
 #pragma unroll
-      for (int e = 0; e < EPS; ++e) fma_p(e);
+      for (int e = 0; e < 2 * EPS; ++e) fma_p(e);
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, NSLOT>([&](auto kk) __attribute__((always_inline)) {
         constexpr int k = decltype(kk)::value;
+        if constexpr (k == TOP) {
+          top();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (k < NPV) {
           // P.V of tile j-1 (zeros before the first tile)
           constexpr int f = k / QB, X = k % QB, kc = f / DB, db = f % DB;
-          if constexpr (X == 0) wait_lgkm<Sch::vwait(f)>();
-          mfma_pv(O[X][db], vf[kc][db], P[X][kc]);
+          mfma_pv(O[X][db], vf[kc][db], Pc[X][kc]);
           // This slot's exp waits for the MFMA issue (the compiler would put
           // the quarter-rate exp first and hold the MFMA up behind it).
 #pragma unroll
@@ -515,9 +559,10 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
         } else {
           // scores of tile j+1 (computed on stale data past the piece's last tile, then unused)
           constexpr int c = (k - NPV) / QB, X = (k - NPV) % QB;
-          if constexpr (X == 0) {
-            wait_lgkm<Sch::kwait(c)>();
-            lds_tie(kf[c]);
+          if constexpr (k == NPV) {
+            wait_lgkm<0>();
+#pragma unroll
+            for (int cc = 0; cc < KC; ++cc) lds_tie(kf[cc]);
           }
           if constexpr (c == 0)
             Sn[X] = mfma_s_first(kf[c], qf[X][c]);
@@ -533,26 +578,14 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
               vh[h][kc][db] = lds_read_v<((4 * kc + h) * DG + 2 * db) * 128>(vc);
           });
         });
-        // Steady state: this wave's copies of the refilled tile, spread over the slots.
-        if constexpr (STEADY) {
-          static_for<0, CPW>([&](auto ii) __attribute__((always_inline)) {
-            constexpr int i = decltype(ii)::value;
-            if constexpr (1 + i * (NSLOT / CPW) == k) {
-              if constexpr (i < KPW)
-                copy16_to_lds_at<i * NWAVE * RPB * D * 2>(kq, kofs[i], sb_copy);
-              else
-                copy16_to_lds_at<(TILE + (i - KPW) * NWAVE * RPB * D) * 2>(vq, vofs[i - KPW], sb_copy);
-            }
-          });
-        }
-        // K fragments of tile j+1
+        // K fragments of tile j+1 (after the barrier that published it)
         static_for<0, KC>([&](auto cc) __attribute__((always_inline)) {
           constexpr int c = decltype(cc)::value;
           if constexpr (Sch::kslot(c) == k) kf[c] = lds_read_k(kn, kaddr[c]);
         });
 #pragma unroll
         for (int e = 0; e < EPS; ++e) {
-          if (k + 1 < NSLOT) fma_p((k + 1) * EPS + e);
+          if (k + 2 < NSLOT) fma_p((k + 2) * EPS + e);
           pr[k * EPS + e] = fast_exp2(xs[k * EPS + e]);
           if (k >= 1) sum_p((k - 1) * EPS + e);
         }
@@ -566,63 +599,11 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
 #pragma unroll
       for (int e = 0; e < EPS; ++e) sum_p((NSLOT - 1) * EPS + e);
 #pragma unroll
-      for (int X = 0; X < QB; ++X)
+      for (int X = 0; X < QB; ++X) {
+        lsp[X] = ps[X];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
           Pn[X][kc] = __builtin_bit_cast(bf16x8, u32x4{pk[X][kc][0], pk[X][kc][1], pk[X][kc][2], pk[X][kc][3]});
-
-      float ls[QB];
-      bool need = false;
-#pragma unroll
-      for (int X = 0; X < QB; ++X) {
-        ls[X] = (ps[X][0] + ps[X][1]) + (ps[X][2] + ps[X][3]);
-        need |= !(ls[X] <= 256.0f) || m[X] == -__builtin_inff();
-      }
-      // The sum bounds every term: while it stays <= 256 the stored max can
-      // stay. Otherwise (and while m is -inf) take the exact row max over both
-      // half-rows; if it exceeds m by more than 8, raise m, rescale l and O,
-      // and recompute the tile's probabilities. The scores of tile j are
-      // recomputed from its K tile, still in LDS (its stage is refilled two
-      // tiles later).
-      if (__any(need)) {
-        f32x16 Sj[QB];
-        wait_lgkm<0>();
-        scores_of(Sj, j);
-#pragma unroll
-        for (int X = 0; X < QB; ++X) {
-          float mx = Sj[X][0];
-#pragma unroll
-          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, Sj[X][v]);
-          mx = half_max(mx) * a.scale_log2;
-          if (__any(mx > m[X] + 8.0f)) {
-            const float mn = fmaxf(m[X], mx);
-            const float alpha = m[X] == -__builtin_inff() ? 0.f : fast_exp2(m[X] - mn);
-            m[X] = mn;
-            l[X] *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              o_fence(O[X][db]);
-              O[X][db] *= alpha;
-              o_fence(O[X][db]);
-            }
-            const float nmx = mn == -__builtin_inff() ? 0.f : -mn;
-            float q4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float p = fast_exp2(fmaf(Sj[X][v], a.scale_log2, nmx));
-              q4[v & 3] += p;
-              Pn[X][v >> 3][v & 7] = (__bf16)p;
-            }
-            ls[X] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
-          }
-        }
-      }
-#pragma unroll
-      for (int X = 0; X < QB; ++X) {
-        l[X] += ls[X];
-        S[X] = Sn[X];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) P[X][kc] = Pn[X][kc];
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
@@ -630,18 +611,32 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
         for (int db = 0; db < DB; ++db)
           vf[kc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vh[0][kc][db], vh[1][kc][db], 0, 1, 2, 3, 4,
                                                                            5, 6, 7));
-      // Masks of tile j+1 (known now that its scores are; never needed in the steady state).
-      if constexpr (!STEADY)
-        if (j + 1 >= jm && j + 1 < n) mask_scores(S, j + 1);
-      st_c = st_n;
-      st_n = st_n + 1 == NS ? 0 : st_n + 1;
-      kq = kp + (size_t)(tile0 + issued) * NK * D;
-      vq = vp + (size_t)(tile0 + issued) * NK * D;
+      // Masks of tile j+1 (known now that its scores are).
+      if (j + 1 >= jm && j + 1 < n) mask_scores(Sn, j + 1);
+      op = oc;
+      oc = on;
+      on = rot(on);
+      ocp = rot(ocp);
     };
-    for (int j = 0; j < n;) {
-      step(std::false_type{}, j);
-      ++j;
+    // Tiles in pairs (an odd count starts with a single tile and one copy).
+    f32x16 S1[QB];
+    bf16x8 P1[QB][2];
+    int j = 0;
+    if (n & 1) {
+      step(0, S, S1, P, P1);
+#pragma unroll
+      for (int X = 0; X < QB; ++X) {
+        S[X] = S1[X];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) P[X][kc] = P1[X][kc];
+      }
+      j = 1;
     }
+    for (; j < n; j += 2) {
+      step(j, S, S1, P, P1);
+      step(j + 1, S1, S, P1, P);
+    }
+    check(n - 1, P, lsp, op);
     // P.V of the last tile.
     wait_lgkm<0>();
 #pragma unroll
