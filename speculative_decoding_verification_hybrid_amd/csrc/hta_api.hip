@@ -68,7 +68,8 @@ int validate(const hta_config_t* c) {
 // blocks would leave a wave count that is not 1, 2 or 4); more rows than
 // one workgroup holds go to further row groups (grid.y). The plan takes qb = 2
 // whenever there are two blocks or more, so every K / V fragment read from LDS
-// feeds two MFMAs; qb = 1 is taken on request or for a single block.
+// feeds two MFMAs; qb = 1 is taken on request or for a single block, and at
+// D = 128 it may use up to 8 waves (two per SIMD, accumulators in VGPRs).
 // VALU path: 16 rows per workgroup. DOT path: all M rows in one workgroup of
 // 4 waves.
 void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) {
@@ -77,11 +78,12 @@ void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) 
     pl->tile_tokens = hta::kMfmaTileTokens;
     const int nqb = (d.M + 31) / 32;
     const int qb = qb_req > 0 ? qb_req : (nqb >= 2 ? 2 : 1);
-    const int max_blocks = 4 * qb;              // blocks per workgroup
+    const int max_waves = qb == 1 && d.D == 128 ? 8 : 4;  // qb = 1 at D = 128: up to two waves per SIMD
+    const int max_blocks = max_waves * qb;      // blocks per workgroup
     const int rg = (nqb + max_blocks - 1) / max_blocks;
     const int per = (nqb + rg - 1) / rg;        // blocks per row group
     int waves = (per + qb - 1) / qb;
-    waves = waves <= 1 ? 1 : waves <= 2 ? 2 : 4;
+    waves = waves <= 1 ? 1 : waves <= 2 ? 2 : waves <= 4 ? 4 : 8;
     pl->row_groups = rg;
     pl->rows_per_group = per * 32;
     pl->waves = waves;

@@ -109,6 +109,10 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
   constexpr int NSLOT = NPV + NSC;
   constexpr int EPS = 16 * QB / NSLOT;     // probabilities per slot
   using Sch = SlotSchedule<D, QB>;
+  // Two waves per SIMD (eight per workgroup) leave each wave half the
+  // register file: the P.V accumulators and Q then live in VGPRs with
+  // compiler-visible MFMAs; with one wave per SIMD they sit in AGPRs.
+  constexpr bool VACC = NWAVE == 8;
   static_assert(NBLK % NWAVE == 0, "copies split evenly over the waves");
   static_assert(EPS * NSLOT == 16 * QB, "slot layout");
   static_assert(NS >= 4, "stages: tiles j-1, j, j+1 in use plus one in flight");
@@ -392,7 +396,8 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
 #pragma unroll
     for (int X = 0; X < QB; ++X)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) q_tie(qf[X][c]);
+      for (int c = 0; c < KC; ++c)
+        if constexpr (!VACC) q_tie(qf[X][c]);
     scores_of(S, 0u, 0);
     // The stored max starts at tile 0's exact row max (so the first tile needs
     // no rescaling pass); rows that see nothing in tile 0 keep -inf. The
@@ -458,9 +463,9 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
             l[X] *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-              o_fence(O[X][db]);
+              if constexpr (!VACC) o_fence(O[X][db]);
               O[X][db] *= alpha;
-              o_fence(O[X][db]);
+              if constexpr (!VACC) o_fence(O[X][db]);
             }
             float q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -488,8 +493,14 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
 #pragma unroll
       for (int X = 0; X < QB; ++X)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o_tie(O[X][db]);
+        for (int db = 0; db < DB; ++db)
+          if constexpr (!VACC) o_tie(O[X][db]);
       wait_lgkm<0>();  // this wave's V reads of tile j-1
+      // (tied to the wait, for the compiler-visible MFMAs of the VGPR form)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) lds_tie(vf[kc][db]);
       // Top of the tile (after the first TOP P.V MFMAs, which run meanwhile):
       // tile j+1 has landed for every wave (each waits for its own copies and
       // the barrier publishes them), and every wave is done with the stage of
@@ -551,7 +562,10 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
         if constexpr (k < NPV) {
           // P.V of tile j-1 (zeros before the first tile)
           constexpr int f = k / QB, X = k % QB, kc = f / DB, db = f % DB;
-          mfma_pv(O[X][db], vf[kc][db], Pc[X][kc]);
+          if constexpr (VACC)
+            mfma_pv_v(O[X][db], vf[kc][db], Pc[X][kc]);
+          else
+            mfma_pv(O[X][db], vf[kc][db], Pc[X][kc]);
           // This slot's exp waits for the MFMA issue (the compiler would put
           // the quarter-rate exp first and hold the MFMA up behind it).
 #pragma unroll
@@ -640,13 +654,22 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     // P.V of the last tile.
     wait_lgkm<0>();
 #pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) lds_tie(vf[kc][db]);
+#pragma unroll
     for (int f = 0; f < 2 * DB; ++f)
 #pragma unroll
-      for (int X = 0; X < QB; ++X) mfma_pv_after_valu(O[X][f % DB], vf[f / DB][f % DB], P[X][f / DB]);
+      for (int X = 0; X < QB; ++X)
+        if constexpr (VACC)
+          mfma_pv_v(O[X][f % DB], vf[f / DB][f % DB], P[X][f / DB]);
+        else
+          mfma_pv_after_valu(O[X][f % DB], vf[f / DB][f % DB], P[X][f / DB]);
 #pragma unroll
     for (int X = 0; X < QB; ++X)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o_fence(O[X][db]);
+      for (int db = 0; db < DB; ++db)
+        if constexpr (!VACC) o_fence(O[X][db]);
     __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
     __syncthreads();  // every copy has landed and no wave reads the tile buffers any more
 
@@ -704,6 +727,7 @@ struct Inst {
 };
 constexpr int kNsLarge = 9;  // 144 KB of 16 KB stages (D = 128)
 const Inst kInst[] = {
+    {128, 1, 8, kNsLarge, prefix_mfma_kernel<128, 1, 8, kNsLarge>},
     {128, 2, 4, kNsLarge, prefix_mfma_kernel<128, 2, 4, kNsLarge>},
     {128, 2, 2, kNsLarge, prefix_mfma_kernel<128, 2, 2, kNsLarge>},
     {128, 2, 1, kNsLarge, prefix_mfma_kernel<128, 2, 1, kNsLarge>},

@@ -109,6 +109,11 @@ __device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& k, const bf1
 __device__ __forceinline__ void mfma_pv(f32x16& o, const bf16x8& v, const bf16x8& p) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
 }
+// The same with the accumulator in VGPRs, as a compiler-visible MFMA (the
+// compiler inserts the wait states its operands and result need).
+__device__ __forceinline__ void mfma_pv_v(f32x16& o, const bf16x8& v, const bf16x8& p) {
+  o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p, o, 0, 0, 0);
+}
 // Keeps an accumulator in AGPRs at this point (no code).
 __device__ __forceinline__ void o_tie(f32x16& o) { asm volatile("" : "+a"(o)); }
 // The same with 3 wait states ahead of it, for places where the compiler may

@@ -160,7 +160,7 @@ def test_lds_reads_untouched_until_waited():
         n, bad = check_kernel(lines)
         n_inst += 1
         assert n > 0 and not bad, f"D={m.group(2)} QB={m.group(3)} waves={m.group(4)}: {bad[:4]}"
-    assert n_inst == 12
+    assert n_inst == 13
 
 
 def test_checker_catches_early_use():
@@ -309,8 +309,10 @@ def test_asm_mfma_results_not_touched_early():
     for m, tagged in _kernels_tagged("prefix_mfma.hip"):
         n, bad = check_mfma_hazards(tagged)
         n_inst += 1
-        assert n > 0 and not bad, f"D={m.group(2)} QB={m.group(3)} waves={m.group(4)}: {bad[:4]}"
-    assert n_inst == 12
+        # eight waves keep the P.V accumulators in VGPRs with compiler-visible MFMAs
+        vgpr_form = int(m.group(4)) == 8
+        assert (n == 0 if vgpr_form else n > 0) and not bad, f"D={m.group(2)} QB={m.group(3)} waves={m.group(4)}: {bad[:4]}"
+    assert n_inst == 13
 
 
 def test_mfma_hazard_checker_catches_early_reads():

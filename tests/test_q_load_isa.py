@@ -77,7 +77,7 @@ def check_kernel(body):
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-@pytest.mark.parametrize("src,instances", [("prefix_mfma.hip", 12)])
+@pytest.mark.parametrize("src,instances", [("prefix_mfma.hip", 13)])
 def test_q_fragment_loads_untouched_until_waited(tmp_path, src, instances):
     out = tmp_path / (src + ".s")
     cmd = [_build.hipcc()] + _build.flags_for(src) + ["--cuda-device-only", "-S", os.path.join(_build.CSRC, src),
