@@ -90,7 +90,8 @@ enum hta_device_status {
   HTA_STATUS_BAD_TREE = 1,
   HTA_STATUS_BAD_PREFIX = 2,
   HTA_STATUS_COMMIT_OVERFLOW = 4, /* hta_commit: prefix_len + accept_len would pass kv_capacity */
-  HTA_STATUS_BAD_PATH = 8         /* hta_commit: an accept_path entry outside [0, T) */
+  HTA_STATUS_BAD_PATH = 8,        /* hta_commit: an accept_path entry outside [0, T) */
+  HTA_STATUS_MERGE_TIMEOUT = 16   /* hta_verify_attn: a fused merge gave up waiting (rows NaN) */
 };
 
 /* Prefix-kernel implementation (see hta_plan_t.path). MFMA: bf16 with
@@ -112,6 +113,8 @@ typedef struct {
   int32_t force_path;     /* enum hta_path; AUTO picks MFMA for bf16 with G*T >= 16, DOT for
                              bf16 with D = 128 and G*T <= 8, else VALU */
   int32_t qblocks_per_wave; /* MFMA path: 32-row query blocks per wave, 1 or 2; 0 = planned */
+  int32_t fuse_merge;       /* MFMA path, hta_verify_attn: 1 = merge inside the split-KV launch
+                               (see hta_verify_attn), 0 = separate merge launch (default) */
 } hta_config_t;
 
 typedef struct {
@@ -146,7 +149,13 @@ HTA_API int hta_get_plan(hta_handle_t h, hta_plan_t* plan);
 /* Full verification attention: prefix part (split-KV over all compute units,
  * no mask) + tree part (ancestor mask) + exact log-sum-exp merge.
  * Layouts and rules as in the header comment. out has the handle's dtype;
- * lse is float32 natural log. LongSpec, "Fast Tree Attention". */
+ * lse is float32 natural log. LongSpec, "Fast Tree Attention".
+ * With config.fuse_merge on the MFMA path (and a grid no wider than the
+ * device) the merge runs inside the split-KV launch: the workgroups of a
+ * (sequence, KV head) wait for each other (bounded; past the bound the rows
+ * come out NaN with HTA_STATUS_MERGE_TIMEOUT, which hta_get_status also
+ * recovers from), so that launch needs the whole device to itself while it
+ * runs. Calls on one handle must not overlap. */
 HTA_API int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
                     const void* k_tree, const void* v_tree, const int32_t* parent,
                     const int32_t* prefix_len, void* out, float* lse, void* stream);

@@ -32,6 +32,7 @@ constexpr int kStatusBadTree = 1;
 constexpr int kStatusBadPrefix = 2;
 constexpr int kStatusCommitOverflow = 4;
 constexpr int kStatusBadPath = 8;
+constexpr int kStatusMergeTimeout = 16;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

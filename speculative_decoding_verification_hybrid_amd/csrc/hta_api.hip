@@ -22,6 +22,9 @@ struct hta_handle_s {
   unsigned* seq_count;              // [B] arrival counters of hta_commit; zero between calls
   unsigned long long* topk_part;    // [B * kMaxTreeSplit * (kMaxTreeGuesses + 1)] keys (hta_build_tree)
   int* tree_aux;                    // [2 * B * (kMaxTreeGuesses + 1)] match ends, x1 + guesses
+  int* seg_sync;                    // [2 * B * Hkv * row_groups] fused-merge arrivals / departures
+  int* seg_err;                     // [B * Hkv * row_groups] fused-merge tree checks
+  bool fuse_merge;                  // hta_verify_attn merges inside the split-KV launch
 };
 
 namespace {
@@ -55,6 +58,7 @@ int validate(const hta_config_t* c) {
                                  c->dtype == HTA_BF16))
     return HTA_ERR_UNSUPPORTED;
   if (c->qblocks_per_wave < 0 || c->qblocks_per_wave > 2) return HTA_ERR_INVALID_ARG;
+  if (c->fuse_merge != 0 && c->fuse_merge != 1) return HTA_ERR_INVALID_ARG;
   // Index arithmetic limits: rows and per-sequence KV spans stay within int32.
   const int64_t rows = (int64_t)c->batch * c->n_q_heads * c->tree_nodes;
   if (rows * c->head_dim > INT32_MAX) return HTA_ERR_UNSUPPORTED;
@@ -214,6 +218,11 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   off = align256(off + (size_t)d.B * sizeof(unsigned));
   const size_t off_st = off;
   off = align256(off + sizeof(int));
+  const size_t off_ss = off;
+  const int64_t n_seg = (int64_t)d.B * d.Hkv * h->pl.row_groups;
+  off = align256(off + (size_t)n_seg * 2 * sizeof(int));
+  const size_t off_se = off;
+  off = align256(off + (size_t)n_seg * sizeof(int));
   if (hipMalloc(&h->ws, off) != hipSuccess) {
     (void)hipGetLastError();
     delete h;
@@ -223,12 +232,23 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   h->slots.o = base + off_so;
   h->slots.o_bf16 = slot_bf16;
   h->slots.lse2 = reinterpret_cast<float*>(base + off_sl);
+  h->slots.o_bytes = off_sl - off_so;
+  h->slots.lse2_bytes = off_ap - off_sl;
   h->err_b = reinterpret_cast<int*>(base + off_eb);
   h->status = reinterpret_cast<int*>(base + off_st);
   h->argmax_part = reinterpret_cast<unsigned long long*>(base + off_ap);
   h->seq_count = reinterpret_cast<unsigned*>(base + off_ct);
   h->topk_part = reinterpret_cast<unsigned long long*>(base + off_tk);
   h->tree_aux = reinterpret_cast<int*>(base + off_ta);
+  h->seg_sync = reinterpret_cast<int*>(base + off_ss);
+  h->seg_err = reinterpret_cast<int*>(base + off_se);
+  // The fused merge waits for all workgroups of a segment, so every workgroup
+  // of the launch must be resident at once: only when the grid fits the
+  // device (the default plan does; a larger num_workgroups does not).
+  // (The fused merge addresses the slots with 32-bit buffer offsets.)
+  h->fuse_merge = cfg->fuse_merge != 0 && path == HTA_PATH_MFMA &&
+                  (int64_t)h->pl.nwg * h->pl.row_groups <= (int64_t)cus * (occ > 0 ? occ : 1) &&
+                  h->slots.o_bytes < ((size_t)1 << 31);
   if (hipMemset(base + off_eb, 0, off - off_eb) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws);
@@ -278,6 +298,14 @@ int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const vo
   if (!all_aligned(q, k_cache, v_cache, k_tree, v_tree, out)) return HTA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hta::PrefixInputs in = {q, k_cache, v_cache, k_tree, v_tree, parent, prefix_len};
+  if (h->fuse_merge) {
+    hta::FusedMerge fm;
+    fm.out = out;
+    fm.lse = lse;
+    fm.seg_sync = h->seg_sync;
+    fm.seg_err = h->seg_err;
+    return check_hip(hta::launch_prefix_mfma(h->dims, h->pl, in, h->slots, h->err_b, h->status, s, fm));
+  }
   HTA_TRY(launch_split(h, in, s));
   return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg,
                                            hta::tree_tiles_for(h->dims.T, h->pl.tile_tokens), prefix_len, h->slots,
@@ -416,6 +444,10 @@ int hta_get_status(hta_handle_t h, void* stream, int32_t* device_status) {
     return HTA_ERR_HIP;
   HTA_TRY(check_hip(hta::launch_clear_status(h->status, s)));
   if (hipStreamSynchronize(s) != hipSuccess) return HTA_ERR_HIP;
+  // A timed-out fused merge leaves its sync words inconsistent: clear them.
+  if ((v & HTA_STATUS_MERGE_TIMEOUT) &&
+      hipMemset(h->seg_sync, 0, (size_t)h->dims.B * h->dims.Hkv * h->pl.row_groups * 2 * sizeof(int)) != hipSuccess)
+    return HTA_ERR_HIP;
   *device_status = v;
   return HTA_OK;
 }

@@ -26,6 +26,7 @@ struct Slots {
   void* o;
   float* lse2;
   bool o_bf16;
+  size_t o_bytes = 0, lse2_bytes = 0;  // sizes of the two arrays
 };
 
 struct PrefixLaunch {
@@ -55,8 +56,17 @@ struct PrefixInputs {
 // Split-KV kernels: write one partial per (workgroup, segment piece) to slots.
 // With the tree fused in, the workgroup holding the tree tile of (b, KV head 0)
 // writes err_b[b] (1 if parent[] of b is malformed) and raises the status bit.
+// Fused merge of the MFMA kernel (fuse.out != null): final out / lse written
+// by the split-KV launch itself, with per (segment, row group) sync words
+// (two ints, zero between launches) and tree-check words.
+struct FusedMerge {
+  void* out = nullptr;
+  float* lse = nullptr;
+  int* seg_sync = nullptr;
+  int* seg_err = nullptr;
+};
 hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
-                              int* err_b, int* status, hipStream_t s);
+                              int* err_b, int* status, hipStream_t s, const FusedMerge& fuse = FusedMerge());
 hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                               int* err_b, int* status, hipStream_t s);
 // Small-M bf16 split-KV kernel (v_dot2 + DPP; D = 128, at most kDotMaxRows

@@ -1,24 +1,13 @@
-// Log-sum-exp merge of partial attentions (LongSpec summary pages, "Fast
-// Tree Attention": the cached and speculative parts are aggregated with the
-// log-sum-exp trick, which keeps the result exact).
-//
-// For one output row with partials (o_k normalised, lse_k) over disjoint key
-// sets: lse = log2(sum_k 2^lse_k) and out = sum_k 2^(lse_k - lse) o_k. Parts
-// with lse_k = -inf contribute nothing; a row with no part at all gets
-// out = 0, lse = -inf. Internally every LSE is base 2; the stored lse is
-// natural log.
-//
-// One wave per output row. Its 64 lanes are PG part groups x (D/8) lanes of
-// 8 dims: part group p takes parts p, p+PG, p+2PG, ... and keeps its own
-// running max and weighted sum, so each lane has up to 8 independent loads in
-// flight; the groups are then combined with cross-lane exchanges.
+// Merge kernel: the log-sum-exp merge of partial attentions (merge_row.h)
+// as its own launch, one wave per output row, over either the slots of one
+// split-KV launch (each (sequence, KV head) segment's partials are the slots
+// of the workgroups that own its tiles) or caller-provided part arrays.
 #include "common.h"
 #include "hta_internal.h"
+#include "merge_row.h"
 
 namespace hta {
 namespace {
-
-constexpr int UNROLL = 8;
 
 struct MergeArgs {
   // slot mode: partials of one split-KV launch
@@ -38,27 +27,10 @@ struct MergeArgs {
   int B, Hq, Hkv, G, T, Lcap, M;
 };
 
-// 8 consecutive elements of a partial row as floats.
-__device__ __forceinline__ void load8(const float* p, float* o) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-  o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
-  o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
-}
-__device__ __forceinline__ void load8(const unsigned short* p, float* o) {
-  const u32x4 a = *(const u32x4*)p;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = __uint_as_float(a[i] << 16);
-    o[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
-  }
-}
-
 template <int D, bool SLOTS, typename TSlot, bool OUT_BF16>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  constexpr int LPR = D / 8;   // lanes per part group (8 dims each)
-  constexpr int PG = 64 / LPR;  // part groups per row
+  constexpr int LPR = D / 8;  // lanes per part group (8 dims each)
   const int lane = threadIdx.x & 63;
-  const int pg = lane / LPR;
   const int dl = lane % LPR;
   const int64_t rows_total = (int64_t)a.B * a.Hq * a.T;
   // Rows are ordered (b, head, node), so a (sequence, KV head) segment's rows
@@ -129,93 +101,17 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     l_scale = kLog2e;
   }
 
-  // This lane's part group: running max m, weighted sum s and accumulator acc.
-  float m = -__builtin_inff(), s = 0.f, acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int k0 = pg; k0 < p_count; k0 += PG * UNROLL) {
-    float lk[UNROLL], ov[UNROLL][8];
-    // Which of this step's parts hold nothing (past the end, or a workgroup
-    // that owns no tile) is known before any load, so every load of the step
-    // is issued before the first wait.
-    bool dead[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      dead[u] = k0 + u * PG >= p_count;
-      if (SLOTS && maybe_empty) {
-        const unsigned wk = w_first + (unsigned)min(k0 + u * PG, p_count - 1);
-        dead[u] = dead[u] || split_begin(wk, a.nwg, TT) == split_begin(wk + 1, a.nwg, TT);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int k = min(k0 + u * PG, p_count - 1);  // in-bounds; ignored past the end
-      lk[u] = l_base[(size_t)k * l_stride];
-      load8(o_base + (size_t)k * o_stride, ov[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) lk[u] = dead[u] ? -__builtin_inff() : lk[u] * l_scale;
-    // No branch on the loaded values: while every part so far is empty, m and
-    // mc are -inf, alpha is 0 and every weight is 0, so s and acc stay 0.
-    float mc = m;
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) mc = fmaxf(mc, lk[u]);
-    const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mc);
-    s *= alpha;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const bool live = lk[u] != -__builtin_inff();  // an empty part's o is never used
-      const float wk = live ? fast_exp2(lk[u] - mc) : 0.f;
-      s += wk;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += live ? wk * ov[u][e] : 0.f;
-    }
-    m = mc;
-  }
-  // Combine the part groups (lanes dl, dl + LPR, ... hold the same dims).
-  float mt = m;
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-  const float sc = (m == -__builtin_inff()) ? 0.f : fast_exp2(m - mt);
-  s *= sc;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] *= sc;
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-    s += __shfl_xor(s, off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
-  }
-  float lse_out;
-  if (mt == -__builtin_inff()) {
-    lse_out = -__builtin_inff();
+  auto load_o = [&](int k, float* v) { merge_load8(o_base + (size_t)k * o_stride, v); };
+  auto load_l = [&](int k) { return l_base[(size_t)k * l_stride] * l_scale; };
+  if (SLOTS && maybe_empty) {
+    const unsigned nwg = (unsigned)a.nwg;
+    merge_row<D, OUT_BF16>(
+        lane, p_count, load_o, load_l,
+        [&](int k) { return split_begin(w_first + (unsigned)k, nwg, TT) == split_begin(w_first + (unsigned)k + 1, nwg, TT); },
+        bad, a.out, a.lse, row);
   } else {
-    const float inv = 1.0f / s;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= inv;
-    lse_out = (mt + fast_log2(s)) * kLn2;
+    merge_row<D, OUT_BF16>(lane, p_count, load_o, load_l, [](int) { return false; }, bad, a.out, a.lse, row);
   }
-  if (bad) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __builtin_nanf("");
-    lse_out = __builtin_nanf("");
-  }
-  if (pg != 0) return;
-  if (OUT_BF16) {
-    u32x4 pk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pk[i] = (unsigned)float_to_bf16_bits(acc[2 * i]) | ((unsigned)float_to_bf16_bits(acc[2 * i + 1]) << 16);
-    *(u32x4*)(static_cast<unsigned short*>(a.out) + (size_t)row * D + dl * 8) = pk;
-  } else {
-    float* op = static_cast<float*>(a.out) + (size_t)row * D + dl * 8;
-    f32x4 v0 = {acc[0], acc[1], acc[2], acc[3]}, v1 = {acc[4], acc[5], acc[6], acc[7]};
-    *(f32x4*)op = v0;
-    *(f32x4*)(op + 4) = v1;
-  }
-  if (dl == 0) a.lse[row] = lse_out;
 }
 
 typedef void (*MergeFn)(MergeArgs);

@@ -61,6 +61,7 @@
 // sum bounds every term) or m is still -inf, which after a piece's first tile
 // is rare; that check sits after the slots, where it also rescales O.
 #include "hta_internal.h"
+#include "merge_row.h"
 #include "prefix_mfma_common.h"
 
 namespace hta {
@@ -119,9 +120,9 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
   static_assert(NS * STAGE >= NWAVE * 32 * QB * SROW, "epilogue staging fits in the tile buffers");
 
   __shared__ __attribute__((aligned(1024))) unsigned short lds[NS * STAGE];
-  __shared__ int par_s[64];
   __shared__ unsigned long long anc_s[64];
   __shared__ int bad_s;
+  __shared__ int timed_out_s;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,8 +183,11 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
   }
   const unsigned wlds = __builtin_amdgcn_readfirstlane(lds_base + (unsigned)(wave * RPB * D * 2));
 
+  int seg_lo = -1, seg_hi = -1;  // (sequence, KV head) segments this workgroup holds tiles of
   while (true) {
     const int b = sw.b, g = sw.g;
+    if (seg_lo < 0) seg_lo = b * a.Hkv + g;
+    seg_hi = b * a.Hkv + g;
     const unsigned s_first = sw.seq_first + (unsigned)(g * sw.nt);
     const int tile0 = (int)(x - s_first);
     const unsigned piece_end = min(x_end, s_first + (unsigned)sw.nt);
@@ -198,22 +202,12 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     const size_t kt_off = (size_t)(b * a.Hkv + g) * a.T * D;
     const unsigned short* qp = a.q + (size_t)(b * a.Hq + g * a.G) * a.T * D;
 
+    // Ancestor words of this sequence's tree (pieces holding tree tiles); the
+    // parent array is loaded with the prologue's copies and Q, the words are
+    // built once those have landed.
     unsigned long long anc[QB];
 #pragma unroll
     for (int X = 0; X < QB; ++X) anc[X] = 0ull;
-    if (has_tree) {
-      if (tid == 0) bad_s = 0;
-      if (tid < a.T) par_s[tid] = a.parent[(size_t)b * a.T + tid];
-      __syncthreads();
-      if (tid < a.T) {
-        bool ok = true;
-        anc_s[tid] = ancestor_word(par_s, tid, &ok);
-        if (!ok) bad_s = 1;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int X = 0; X < QB; ++X) anc[X] = anc_s[okq[X] ? rowq[X] % a.T : 0];
-    }
 
     // Tokens of tile t of the piece that hold keys (>= 1 for every tile).
     auto nvalid_of = [&](int t) __attribute__((always_inline)) {
@@ -360,6 +354,9 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
         qf[X][c] = __builtin_bit_cast(bf16x8, r);
       }
     }
+    int par_r = 0;
+    if (has_tree && tid < a.T)
+      asm volatile("global_load_dword %0, %1, off" : "=v"(par_r) : "v"(a.parent + (size_t)b * a.T + tid) : "memory");
     for (int t = 1; t < min(n, P0); ++t) copy_tile(t);
     wait_ahead(min(n, P0) - 1);
     // Tie the Q registers to the wait: nothing below may read them earlier.
@@ -374,6 +371,37 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
         if (!okq[X]) r = u32x4{0u, 0u, 0u, 0u};
         qf[X][c] = __builtin_bit_cast(bf16x8, r);
       }
+    if (has_tree) {
+      asm volatile("" : "+v"(par_r));  // landed with the copies waited for above
+      // Ancestor words by pointer doubling in wave 0 (node i in lane i, T <= 64):
+      // after round r a node's word holds its ancestors up to distance 2^r - 1
+      // and p its ancestor at distance 2^r, so 6 rounds cover any depth. The
+      // tree is valid iff every node has -1 <= parent < its own index.
+      if (wave == 0) {
+        const bool node = lane < a.T;
+        int p = node ? par_r : -1;
+        const bool ok = !node || (p >= -1 && p < lane);
+        unsigned long long an = node ? 1ull << lane : 0ull;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+          const int src = p >= 0 && p < 64 ? p : lane;
+          const int pp = __shfl(p, src);
+          const unsigned lo = __shfl((unsigned)an, src), hi = __shfl((unsigned)(an >> 32), src);
+          if (src != lane) {
+            an |= ((unsigned long long)hi << 32) | lo;
+            p = pp;
+          }
+        }
+        if (node) anc_s[lane] = ok ? an : 1ull << lane;
+        const bool bad_tree = __any(!ok);
+        if (lane == 0) bad_s = bad_tree;
+      }
+      // (LDS-only wait before the barrier: tile 1's copies stay in flight)
+      wait_lgkm<0>();
+      tile_barrier();
+#pragma unroll
+      for (int X = 0; X < QB; ++X) anc[X] = anc_s[okq[X] ? rowq[X] % a.T : 0];
+    }
     tile_barrier();
     // Scores of the tile in the stage at LDS byte offset kb, straight from its
     // K tile in LDS (prologue and the rare recomputation of the max-raise path);
@@ -428,6 +456,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     auto rot = [](unsigned o) __attribute__((always_inline)) { return o + SB == NS * SB ? 0u : o + SB; };
     unsigned op = 0u, oc = 0u, on = rot(0u);  // stage byte offsets of tiles j-1, j and j+1
     unsigned ocp = (unsigned)((NS - 2) % NS) * SB;  // stage byte offset of tile j-2+NS
+    bool drained = false;                           // every copy of the piece has landed and been published
     // Probability sum of tile j-1, checked (and added to l) at the start of tile j.
     float lsp[QB];
 #pragma unroll
@@ -518,6 +547,14 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
           ++issued;
           kq += NK * D;
           vq += NK * D;
+        } else if (issued == n) {
+          // Nothing left to queue: once every copy has landed and one barrier
+          // has published them, the remaining tiles need neither.
+          if (!drained) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only<0>());
+            tile_barrier();
+            drained = true;
+          }
         } else {
           wait_ahead(issued - j - 2);
           tile_barrier();
@@ -693,7 +730,14 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
                   ((unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 3] * inv) << 16);
           *(u32x2*)(stg + (32 * X + l32) * SROW + d) = pk;
         }
-      if (okq[X] && hh == 0) a.slot_lse2[(size_t)slot * a.M + rowq[X]] = m[X] + fast_log2(lt);
+      if (okq[X] && hh == 0) {
+        const float v = m[X] + fast_log2(lt);
+        if (a.fuse)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), slot_rsrc(a.slot_lse2, a.slot_bytes_l),
+                                                (unsigned)(slot * a.M + rowq[X]) * 4u, 0, kCpolDevice);
+        else
+          a.slot_lse2[(size_t)slot * a.M + rowq[X]] = v;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -701,18 +745,135 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
       const int u = i * 64 + lane;
       const int rr = u / DCH, c = u % DCH;
       const u32x4 val = *(const u32x4*)(stg + rr * SROW + c * 8);
-      if (wrow0 + rr < row_limit) *(u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8) = val;
+      if (wrow0 + rr < row_limit) {
+        if (a.fuse)
+          __builtin_amdgcn_raw_buffer_store_b128(val, slot_rsrc(a.slot_o, a.slot_bytes_o),
+                                                 ((unsigned)(slot * a.M + wrow0 + rr) * D + (unsigned)c * 8) * 2u, 0,
+                                                 kCpolDevice);
+        else
+          *(u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8) = val;
+      }
     }
-    // The workgroup holding the first tree tile of (b, KV head 0) reports the tree check.
+    // The workgroup holding the first tree tile of (b, KV head 0) reports the
+    // tree check; for the fused merge, each segment's holder notes it too.
     if (has_tree && tile0 <= n_prefix && g == 0 && blockIdx.y == 0 && tid == 0) {
       a.err_b[b] = bad_s;
       if (bad_s) atomicOr(a.status, kStatusBadTree);
     }
+    if (a.fuse && has_tree && tile0 <= n_prefix && tid == 0)
+      __hip_atomic_store(a.seg_err + (b * a.Hkv + g) * (int)gridDim.y + (int)blockIdx.y, bad_s, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
 
     x = piece_end;
     if (x >= x_end) break;
     if (!walk_next(&sw, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles)) break;
-    __syncthreads();  // staging area, par_s / anc_s / bad_s of this piece are no longer read
+    __syncthreads();  // staging area, anc_s / bad_s of this piece are no longer read
+  }
+
+  // Fused merge (verification attention, where every segment has tiles):
+  // the workgroups holding tiles of a segment each merge a contiguous share
+  // of its rows once all of them have left their partials. Each publishes
+  // its partials (release), counts itself in every segment it holds, then per
+  // segment waits until the count is complete -- every contributor is resident
+  // (one launch no wider than the device), and the wait is bounded: past the
+  // bound the share's rows come out NaN with HTA_STATUS_MERGE_TIMEOUT -- and
+  // merges its rows (merge_row.h) from all contributors' slots. The last
+  // contributor past the wait clears the segment's words for the next launch.
+  if (a.fuse) {
+    constexpr int kSpinLimit = 1 << 15;  // about 40 ms of polling
+    const int RG = (int)gridDim.y;
+    // The partials went out as device-coherent (write-through) stores: once
+    // they are complete, every other workgroup's sc1 loads see them.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      for (int sg = seg_lo; sg <= seg_hi; ++sg)
+        __hip_atomic_fetch_add(a.seg_sync + 2 * (sg * RG + (int)blockIdx.y), 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    const int rows_lo = (int)blockIdx.y * a.rows_per_group;
+    const int nrows = row_limit - rows_lo;
+    const bool maybe_empty = TT < (unsigned)a.nwg;
+    const __amdgpu_buffer_rsrc_t rs_o = slot_rsrc(a.slot_o, a.slot_bytes_o);
+    const __amdgpu_buffer_rsrc_t rs_l = slot_rsrc(a.slot_lse2, a.slot_bytes_l);
+    for (int sg = seg_lo; sg <= seg_hi; ++sg) {
+      const int b = sg / a.Hkv, g = sg % a.Hkv;
+      unsigned first;
+      int count;
+      segment_tiles(a.prefix_len, a.Hkv, a.Lcap, NK, a.tree_tiles, b, g, &first, &count);
+      const unsigned w_first = split_owner(first, (unsigned)a.nwg, TT);
+      const unsigned w_last = split_owner(first + (unsigned)count - 1, (unsigned)a.nwg, TT);
+      const int n_range = (int)(w_last - w_first) + 1;  // slots of the segment (some empty when TT < nwg)
+      // Contributors (workgroups owning tiles of the segment) and this one's
+      // rank among them: with fewer tiles than workgroups some in the range
+      // own none and never arrive.
+      int nc = n_range, share = (int)((unsigned)w - w_first);
+      if (maybe_empty) {
+        nc = 0;
+        share = 0;
+        for (unsigned u = w_first; u <= w_last; ++u) {
+          const int ne = split_begin(u, (unsigned)a.nwg, TT) < split_begin(u + 1, (unsigned)a.nwg, TT);
+          nc += ne;
+          if (u < (unsigned)w) share += ne;
+        }
+      }
+      int* sync = a.seg_sync + 2 * (sg * RG + (int)blockIdx.y);
+      if (tid == 0) {
+        int it = 0;
+        while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nc && it < kSpinLimit) {
+          __builtin_amdgcn_s_sleep(2);
+          ++it;
+        }
+        timed_out_s = it >= kSpinLimit;
+        if (timed_out_s) atomicOr(a.status, kStatusMergeTimeout);
+        if (__hip_atomic_fetch_add(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nc - 1) {
+          __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(sync + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+      const int Lraw = a.prefix_len[b];
+      const bool bad_prefix = Lraw < 0 || Lraw > a.Lcap;
+      const bool bad = timed_out_s || bad_prefix ||
+                       __hip_atomic_load(a.seg_err + sg * RG + (int)blockIdx.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      const int p_first = (int)w_first + b * a.Hkv + g;
+      // This workgroup's rows, RB per wave at a time (rows of a wave batch
+      // past the share are skipped: their loads are in bounds, their results
+      // unused).
+      constexpr int RB = 2, UNR = kMergeUnroll;  // the merge kernel's passes: the same bits
+      const int r_beg = rows_lo + share * nrows / nc, r_end = rows_lo + (share + 1) * nrows / nc;
+      if (bad_prefix && g == 0 && r_beg == 0 && tid == 0) atomicOr(a.status, kStatusBadPrefix);
+      for (int r0 = r_beg + wave * RB; r0 < r_end; r0 += NWAVE * RB) {
+        int64_t row[RB];
+        unsigned o_off[RB], l_off[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int r = min(r0 + rb, r_end - 1);
+          row[rb] = r0 + rb < r_end ? ((int64_t)b * a.Hq + g * a.G + r / a.T) * a.T + r % a.T : -1;
+          // Device-coherent loads (sc1) of the slots other workgroups wrote through.
+          o_off[rb] = ((unsigned)(p_first * a.M + r) * D + (unsigned)(lane % (D / 8)) * 8) * 2u;
+          l_off[rb] = (unsigned)(p_first * a.M + r) * 4u;
+        }
+        auto load_o = [&](int rb, int k) {
+          return __builtin_amdgcn_raw_buffer_load_b128(rs_o, o_off[rb] + (unsigned)k * (unsigned)(a.M * D * 2), 0,
+                                                       kCpolDevice);
+        };
+        auto load_l = [&](int rb, int k) {
+          return __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rs_l, l_off[rb] + (unsigned)k * (unsigned)(a.M * 4), 0,
+                                                          kCpolDevice));
+        };
+        if (maybe_empty) {
+          const unsigned nwg = (unsigned)a.nwg;
+          merge_rows<D, RB, UNR, true>(
+              lane, n_range, load_o, load_l,
+              [&](int k) { return split_begin(w_first + (unsigned)k, nwg, TT) == split_begin(w_first + (unsigned)k + 1, nwg, TT); },
+              bad, a.out, a.lse, row);
+        } else {
+          merge_rows<D, RB, UNR, true>(lane, n_range, load_o, load_l, [](int) { return false; }, bad, a.out, a.lse, row);
+        }
+      }
+      __syncthreads();  // timed_out_s is rewritten for the next segment
+    }
   }
 }
 
@@ -766,7 +927,7 @@ int prefix_mfma_occupancy(int D, int waves, int qb) {
 }
 
 hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
-                              int* err_b, int* status, hipStream_t s) {
+                              int* err_b, int* status, hipStream_t s, const FusedMerge& fuse) {
   const mfma::Inst* inst = mfma::find(d.D, pl.qb, pl.waves);
   if (!inst) return hipErrorInvalidValue;
   PrefixArgs a;
@@ -792,6 +953,13 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
   a.rows_per_group = pl.rows_per_group;
   a.tree_tiles = in.k_tree ? tree_tiles_for(d.T, mfma::NK) : 0;
   a.scale_log2 = d.scale_log2;
+  a.fuse = fuse.out != nullptr && in.k_tree != nullptr;
+  a.out = fuse.out;
+  a.lse = fuse.lse;
+  a.seg_sync = fuse.seg_sync;
+  a.seg_err = fuse.seg_err;
+  a.slot_bytes_o = (unsigned)slots.o_bytes;
+  a.slot_bytes_l = (unsigned)slots.lse2_bytes;
   hipLaunchKernelGGL(inst->fn, dim3(pl.nwg, pl.row_groups), dim3(pl.waves * 64), 0, s, a);
   return hipGetLastError();
 }

@@ -30,7 +30,28 @@ struct PrefixArgs {
   int B, Hq, Hkv, G, T, Lcap, M;
   int nwg, rows_per_group, tree_tiles;
   float scale_log2;
+  // Fused merge (fuse != 0): final out (bf16) and lse, and per (segment, row
+  // group) words: seg_sync[2 i] arrivals and seg_sync[2 i + 1] departures
+  // (zero between launches), seg_err[i] the segment's tree check.
+  int fuse;
+  void* out;
+  float* lse;
+  int* seg_sync;
+  int* seg_err;
+  unsigned slot_bytes_o, slot_bytes_l;  // slot array sizes (fused merge: buffer loads / stores)
 };
+
+// Cache policy of device-coherent accesses (sc1): stores write through to the
+// point of coherence of the whole device, loads read from it, so workgroups on
+// different XCDs (each with its own L2) see each other's data without
+// cache-wide write-back or invalidation.
+constexpr int kCpolDevice = 16;
+
+// Raw buffer resource over `bytes` bytes at p (out-of-range accesses return 0
+// or are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
 
 // XOR swizzle of the 16-byte chunks of K row r. D = 128: a row spans all 64
 // banks and the swizzle is a bijection of r's low 4 bits, so the 16 rows of a

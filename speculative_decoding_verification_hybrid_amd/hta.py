@@ -36,6 +36,7 @@ HTA_STATUS_BAD_TREE = 1
 HTA_STATUS_BAD_PREFIX = 2
 HTA_STATUS_COMMIT_OVERFLOW = 4
 HTA_STATUS_BAD_PATH = 8
+HTA_STATUS_MERGE_TIMEOUT = 16
 
 HTA_PATH_AUTO = 0
 HTA_PATH_MFMA = 1
@@ -62,6 +63,7 @@ class HtaConfig(ctypes.Structure):
         ("num_workgroups", ctypes.c_int32),
         ("force_path", ctypes.c_int32),
         ("qblocks_per_wave", ctypes.c_int32),
+        ("fuse_merge", ctypes.c_int32),
     ]
 
 
@@ -167,10 +169,10 @@ def hta_status_string(code: int) -> str:
 
 def make_config(*, batch, n_q_heads, n_kv_heads, head_dim, tree_nodes, kv_capacity, dtype="bf16",
                 softmax_scale=0.0, num_workgroups=0, force_path=HTA_PATH_AUTO,
-                qblocks_per_wave=0) -> HtaConfig:
+                qblocks_per_wave=0, fuse_merge=0) -> HtaConfig:
     dt = {"bf16": HTA_BF16, "f32": HTA_F32, HTA_BF16: HTA_BF16, HTA_F32: HTA_F32}[dtype]
     return HtaConfig(batch, n_q_heads, n_kv_heads, head_dim, tree_nodes, kv_capacity, dt,
-                     float(softmax_scale), num_workgroups, force_path, qblocks_per_wave)
+                     float(softmax_scale), num_workgroups, force_path, qblocks_per_wave, fuse_merge)
 
 
 def hta_validate_config(cfg: HtaConfig) -> int:

@@ -330,3 +330,57 @@ def test_mfma_kernel_pieces(qb, nwg):
     assert status == 0
     ref_out, ref_lse = oracle.verify_attn(w)
     assert_close(w, out, lse, ref_out, ref_lse)
+
+
+# ----------------------------------------------------------------------------
+# the merge inside the split-KV launch (config.fuse_merge)
+# ----------------------------------------------------------------------------
+
+FUSED = ["m256", "m160_half_block", "m512_two_groups", "d64_m64", "ragged_t33", "poison_tail", "drift_keys"]
+
+
+@pytest.mark.parametrize("name", FUSED)
+def test_fused_merge_matches_separate_merge(name):
+    """The fused merge reads the same slots in the same order as the merge kernel: same bits."""
+    w = make_custom(seed=zlib.crc32(name.encode()) % 1000, dtype="bf16", **KERNEL_SHAPES[name])
+    say(f"fused merge {name}: separate, then fused")
+    out_s, lse_s, st_s = run_verify(w, force_path=hta.HTA_PATH_MFMA)
+    out_f, lse_f, st_f = run_verify(w, force_path=hta.HTA_PATH_MFMA, fuse_merge=1)
+    assert st_s == 0 and st_f == 0
+    assert np.array_equal(out_f, out_s) and np.array_equal(lse_f, lse_s)
+    ref_out, ref_lse = oracle.verify_attn(w)
+    assert_close(w, out_f, lse_f, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("nwg", [1, 7, 1000])
+def test_fused_merge_pieces_and_repeats(nwg):
+    """Workgroups spanning several segments (and, at 1000, a grid wider than the
+    device, where the separate merge runs); three calls on one handle, so the
+    sync words come back to zero between launches."""
+    w = make_custom(B=4, Hq=32, Hkv=4, D=128, Lcap=1500, T=24, prefix_len=[1500, 64, 999, 1], seed=60 + nwg)
+    say(f"fused merge num_workgroups={nwg}")
+    ref_out, ref_lse = oracle.verify_attn(w)
+    dev = to_device(w)
+    with hta.hta_create(config_for(w, num_workgroups=nwg, force_path=hta.HTA_PATH_MFMA, fuse_merge=1)) as h:
+        for rep in range(3):
+            out, lse, status = run_verify(w, dev=dev, handle=h)
+            assert status == 0, f"call {rep}: status {status}"
+            assert_close(w, out, lse, ref_out, ref_lse)
+
+
+def test_fused_merge_device_errors():
+    """Bad tree and bad prefix_len rows come out NaN with their status bits through the fused merge."""
+    w = make_custom(B=3, Hq=8, Hkv=2, D=128, Lcap=300, T=10, prefix_len=[300, 200, 100], seed=33)
+    w.parent[1, 6] = 8
+    out, lse, status = run_verify(w, force_path=hta.HTA_PATH_MFMA, fuse_merge=1)
+    assert status == hta.HTA_STATUS_BAD_TREE
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    ref_out, ref_lse = oracle.verify_attn(w, batches=[0, 2])
+    assert_close(w, out, lse, ref_out, ref_lse)
+    w = make_custom(B=2, Hq=8, Hkv=2, D=128, Lcap=300, T=10, prefix_len=[300, 100], seed=34)
+    w.prefix_len[1] = 301
+    out, lse, status = run_verify(w, force_path=hta.HTA_PATH_MFMA, fuse_merge=1)
+    assert status == hta.HTA_STATUS_BAD_PREFIX
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    ref_out, ref_lse = oracle.verify_attn(w, batches=[0])
+    assert_close(w, out, lse, ref_out, ref_lse)

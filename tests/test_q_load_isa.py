@@ -23,6 +23,8 @@ import pytest
 from speculative_decoding_verification_hybrid_amd import _build
 
 VMEM = re.compile(r"^\s*(global_|buffer_|flat_|scratch_)(load|store|atomic)")
+# the prologue's inline-asm loads: Q fragments (dwordx4) and the parent word (dword), addressed by a VGPR pair
+LOAD = re.compile(r"^\s*global_load_dword(?:x4)? (v\[\d+:\d+\]|v\d+), v\[\d+:\d+\], off")
 KERNEL = re.compile(r"^(_ZN3hta4mfma12_GLOBAL__N_118prefix_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E\S*):", re.M)
 
 
@@ -36,7 +38,7 @@ def _regs(line):
 
 def check_kernel(body):
     """Returns (number of Q loads, offending lines) for one kernel's instruction lines."""
-    loads = [i for i, l in enumerate(body) if re.match(r"^\s*global_load_dwordx4 v\[", l)]
+    loads = [i for i, l in enumerate(body) if LOAD.match(l)]
     if not loads:
         return 0, ["no Q loads found"]
     pending = {}  # register -> index of the load that writes it
@@ -55,14 +57,13 @@ def check_kernel(body):
                 break
             continue
         if i in loads:
-            d = re.match(r"^\s*global_load_dwordx4 v\[(\d+):(\d+)\], v\[(\d+):(\d+)\]", l)
-            assert d, l
+            d = LOAD.match(l)
             if _regs(l) & set(pending):
                 bad.append(l.strip())
             for j in issued_after:
                 issued_after[j] += 1
             issued_after[i] = 0
-            for r in range(int(d.group(1)), int(d.group(2)) + 1):
+            for r in _regs(d.group(1)):
                 pending[r] = i
             continue
         if _regs(l) & set(pending):
