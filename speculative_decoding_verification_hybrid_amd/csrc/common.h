@@ -64,17 +64,22 @@ __device__ __forceinline__ int valid_prefix(const int* prefix_len, int b, int Lc
 
 __device__ __forceinline__ int tiles_of(int L, int NK) { return (L + NK - 1) / NK; }
 
-// Tiles of each segment of sequence b: its prefix tiles plus tree_tiles (0 or 1).
-__device__ __forceinline__ int seg_tiles(const int* prefix_len, int b, int Lcap, int NK, int tree_tiles) {
-  return tiles_of(valid_prefix(prefix_len, b, Lcap), NK) + tree_tiles;
+// Tiles of each segment of sequence b in the split: its prefix tiles, its
+// tree_tiles tree tiles, then (tree_weight - 1) * tree_tiles empty tiles that
+// stand for the extra cost of the tree tiles (ancestor words, masks), so the
+// workgroup holding them gets fewer prefix tiles. Kernels skip the empty
+// tiles; a segment's last real tile is at index prefix tiles + tree_tiles - 1.
+__device__ __forceinline__ int seg_tiles(const int* prefix_len, int b, int Lcap, int NK, int tree_tiles,
+                                         int tree_weight = 1) {
+  return tiles_of(valid_prefix(prefix_len, b, Lcap), NK) + tree_tiles * tree_weight;
 }
 
 // Tile counts and split arithmetic are 32-bit: the host keeps
 // (largest possible tile count) * nwg below 2^32.
 __device__ inline unsigned total_tiles(const int* prefix_len, int B, int Hkv, int Lcap, int NK,
-                                       int tree_tiles) {
+                                       int tree_tiles, int tree_weight = 1) {
   unsigned t = 0;
-  for (int b = 0; b < B; ++b) t += (unsigned)seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+  for (int b = 0; b < B; ++b) t += (unsigned)seg_tiles(prefix_len, b, Lcap, NK, tree_tiles, tree_weight);
   return t * (unsigned)Hkv;
 }
 
@@ -88,14 +93,15 @@ __device__ __forceinline__ unsigned split_owner(unsigned x, unsigned nwg, unsign
   return ((x + 1) * nwg - 1) / TT;
 }
 
-// Global index of the first tile of segment (b, g), and its tile count.
+// Global index of the first tile of segment (b, g), and its count of real
+// (non-empty) tiles.
 __device__ inline void segment_tiles(const int* prefix_len, int Hkv, int Lcap, int NK, int tree_tiles,
-                                     int b, int g, unsigned* first, int* count) {
+                                     int b, int g, unsigned* first, int* count, int tree_weight = 1) {
   unsigned acc = 0;
-  for (int bb = 0; bb < b; ++bb) acc += (unsigned)seg_tiles(prefix_len, bb, Lcap, NK, tree_tiles);
-  const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+  for (int bb = 0; bb < b; ++bb) acc += (unsigned)seg_tiles(prefix_len, bb, Lcap, NK, tree_tiles, tree_weight);
+  const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles, tree_weight);
   *first = acc * (unsigned)Hkv + (unsigned)(g * nt);
-  *count = nt;
+  *count = nt - tree_tiles * (tree_weight - 1);
 }
 
 // Walks a workgroup's tile range segment by segment.
@@ -106,10 +112,10 @@ struct SegmentWalk {
 
 // Positions the walk on the segment holding global tile x; false if x is past the end.
 __device__ inline bool walk_start(SegmentWalk* sw, unsigned x, const int* prefix_len, int B, int Hkv,
-                                  int Lcap, int NK, int tree_tiles) {
+                                  int Lcap, int NK, int tree_tiles, int tree_weight = 1) {
   unsigned first = 0;
   for (int b = 0; b < B; ++b) {
-    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles, tree_weight);
     const unsigned span = (unsigned)nt * (unsigned)Hkv;
     if (x < first + span) {
       sw->b = b;
@@ -125,12 +131,12 @@ __device__ inline bool walk_start(SegmentWalk* sw, unsigned x, const int* prefix
 
 // Moves to the next segment that has tiles; false if there is none.
 __device__ inline bool walk_next(SegmentWalk* sw, const int* prefix_len, int B, int Hkv, int Lcap, int NK,
-                                 int tree_tiles) {
+                                 int tree_tiles, int tree_weight = 1) {
   if (++sw->g < Hkv) return true;
   sw->g = 0;
   sw->seq_first += (unsigned)sw->nt * (unsigned)Hkv;
   for (int b = sw->b + 1; b < B; ++b) {
-    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles);
+    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles, tree_weight);
     if (nt > 0) {
       sw->b = b;
       sw->nt = nt;

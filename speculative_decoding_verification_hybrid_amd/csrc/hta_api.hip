@@ -31,6 +31,9 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Split weight of a tree tile in the handle's split-KV launches with tree tiles.
+int tree_weight(const hta_handle_s* h) { return h->pl.path == HTA_PATH_MFMA ? hta::kTreeTileWeight : 1; }
+
 int check_hip(hipError_t e) { return e == hipSuccess ? HTA_OK : HTA_ERR_HIP; }
 
 // Tensor arguments are read with 16-byte vector loads.
@@ -187,8 +190,9 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   }
   // The kernels split tiles with 32-bit arithmetic: keep max_tiles * nwg < 2^32.
   const int nk = h->pl.tile_tokens;
-  const int64_t max_tiles =
-      (int64_t)d.B * d.Hkv * ((d.Lcap + nk - 1) / nk + hta::tree_tiles_for(d.T, nk));
+  const int64_t max_tiles = (int64_t)d.B * d.Hkv *
+                            ((d.Lcap + nk - 1) / nk + hta::tree_tiles_for(d.T, nk) *
+                                                          (path == HTA_PATH_MFMA ? hta::kTreeTileWeight : 1));
   if (cfg->num_workgroups <= 0 && nwg > max_tiles) nwg = max_tiles;
   const int64_t nwg_cap = (int64_t)UINT32_MAX / max_tiles;
   if (nwg_cap < 1) {
@@ -308,8 +312,8 @@ int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, const vo
   }
   HTA_TRY(launch_split(h, in, s));
   return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg,
-                                           hta::tree_tiles_for(h->dims.T, h->pl.tile_tokens), prefix_len, h->slots,
-                                           h->err_b, out, h->dims.bf16, lse, h->status, s));
+                                           hta::tree_tiles_for(h->dims.T, h->pl.tile_tokens), tree_weight(h), prefix_len,
+                                           h->slots, h->err_b, out, h->dims.bf16, lse, h->status, s));
 }
 
 int hta_cross_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
@@ -319,7 +323,7 @@ int hta_cross_attn(hta_handle_t h, const void* q, const void* k_cache, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hta::PrefixInputs in = {q, k_cache, v_cache, nullptr, nullptr, nullptr, prefix_len};
   HTA_TRY(launch_split(h, in, s));
-  return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg, 0, prefix_len, h->slots,
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg, 0, 1, prefix_len, h->slots,
                                            nullptr, out, h->dims.bf16, lse, h->status, s));
 }
 
@@ -400,7 +404,7 @@ int hta_merge_prefix(hta_handle_t h, const int32_t* prefix_len, float* o_prefix,
                      void* stream) {
   if (!h || !prefix_len || !o_prefix || !lse_prefix) return HTA_ERR_INVALID_ARG;
   if (!all_aligned(o_prefix)) return HTA_ERR_INVALID_ARG;
-  return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg, 0, prefix_len, h->slots,
+  return check_hip(hta::launch_merge_slots(h->dims, h->pl.tile_tokens, h->pl.nwg, 0, 1, prefix_len, h->slots,
                                            nullptr, o_prefix, false, lse_prefix, h->status,
                                            static_cast<hipStream_t>(stream)));
 }

@@ -12,6 +12,11 @@ constexpr int kMfmaTileTokens = 32;  // prefix tokens per tile of the split (MFM
 
 // Tiles that hold a segment's T tree tokens when the tree part is fused in.
 __host__ __device__ inline int tree_tiles_for(int T, int nk) { return (T + nk - 1) / nk; }
+// Split weight of a tree tile on the MFMA path (in prefix tiles): the
+// workgroup holding a segment's tree tiles also builds the ancestor words and
+// masks them, so each tree tile counts as this many tiles when the tile
+// stream is split (the extra ones are empty tiles the kernels skip).
+constexpr int kTreeTileWeight = 3;
 
 struct Dims {
   int B, Hq, Hkv, G, T, D, Lcap, M;  // M = G*T query rows per KV head
@@ -114,7 +119,8 @@ hipError_t launch_tree_mask(const Dims& d, const int* parent, uint64_t* mask_out
 // Merge of the slots of one split-KV launch (tile_tokens, nwg and
 // tree_tiles as in that launch) into out (float or bf16) and natural-log
 // lse; err_b (may be null) marks sequences whose rows become NaN.
-hipError_t launch_merge_slots(const Dims& d, int tile_tokens, int nwg, int tree_tiles, const int* prefix_len,
+hipError_t launch_merge_slots(const Dims& d, int tile_tokens, int nwg, int tree_tiles, int tree_weight,
+                              const int* prefix_len,
                               Slots slots,
                               const int* err_b, void* out, bool out_bf16, float* lse, int* status,
                               hipStream_t s);

@@ -16,7 +16,7 @@ struct MergeArgs {
   const float* slot_lse2;
   const int* err_b;
   int* status;
-  int nk, nwg, tree_tiles;
+  int nk, nwg, tree_tiles, tree_weight;
   // parts mode: n_parts caller arrays, natural-log lse
   const float* o_parts;
   const float* lse_parts;
@@ -60,16 +60,20 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     // round trip here rather than one per quantity.
     // (a pointer select, not a branch, so the load is not waited on before the loop below)
     const int err_raw = *(a.err_b != nullptr ? a.err_b + b : a.prefix_len + b);
+    // (segments as the split sees them: prefix tiles, tree tiles and the
+    // empty tiles that weigh the tree tiles; count is the real ones)
     unsigned seq_tiles = 0, before = 0;
-    int count = 0, Lraw = 0;
+    int count = 0, span = 0, Lraw = 0;
 #pragma unroll 4
     for (int bb = 0; bb < a.B; ++bb) {
       const int Lb = a.prefix_len[bb];
-      const int nt = tiles_of((Lb < 0 || Lb > a.Lcap) ? 0 : Lb, a.nk) + a.tree_tiles;
+      const int nr = tiles_of((Lb < 0 || Lb > a.Lcap) ? 0 : Lb, a.nk) + a.tree_tiles;
+      const int nt = nr + a.tree_tiles * (a.tree_weight - 1);
       seq_tiles += (unsigned)nt;
       if (bb < b) before += (unsigned)nt;
       if (bb == b) {
-        count = nt;
+        count = nr;
+        span = nt;
         Lraw = Lb;
       }
     }
@@ -77,7 +81,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     bad = bad_prefix || (a.err_b != nullptr && err_raw != 0);
     if (bad_prefix && h == 0 && node == 0 && lane == 0) atomicOr(a.status, kStatusBadPrefix);
     TT = seq_tiles * (unsigned)a.Hkv;
-    const unsigned first = before * (unsigned)a.Hkv + (unsigned)(g * count);
+    const unsigned first = before * (unsigned)a.Hkv + (unsigned)(g * span);
     int p_first = 0;
     if (count > 0) {
       w_first = split_owner(first, a.nwg, TT);
@@ -144,7 +148,8 @@ unsigned grid_for(const Dims& d) {
 
 }  // namespace
 
-hipError_t launch_merge_slots(const Dims& d, int tile_tokens, int nwg, int tree_tiles, const int* prefix_len,
+hipError_t launch_merge_slots(const Dims& d, int tile_tokens, int nwg, int tree_tiles, int tree_weight,
+                              const int* prefix_len,
                               Slots slots, const int* err_b, void* out, bool out_bf16, float* lse, int* status,
                               hipStream_t s) {
   MergeFn k;
@@ -162,6 +167,7 @@ hipError_t launch_merge_slots(const Dims& d, int tile_tokens, int nwg, int tree_
   a.nk = tile_tokens;
   a.nwg = nwg;
   a.tree_tiles = tree_tiles;
+  a.tree_weight = tree_weight;
   a.out = out;
   a.lse = lse;
   hipLaunchKernelGGL(k, dim3(grid_for(d)), dim3(256), 0, s, a);

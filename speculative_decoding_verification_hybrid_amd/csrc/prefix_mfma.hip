@@ -133,13 +133,13 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
   const int gl = lane & 15;
 
   const int w = xcd_remap(blockIdx.x, a.nwg);
-  const unsigned TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles);
+  const unsigned TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles, a.tree_weight);
   if (TT == 0) return;
   unsigned x = split_begin(w, a.nwg, TT);
   const unsigned x_end = split_begin(w + 1, a.nwg, TT);
   if (x >= x_end) return;
   SegmentWalk sw;
-  if (!walk_start(&sw, x, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles)) return;
+  if (!walk_start(&sw, x, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles, a.tree_weight)) return;
 
   const int row_limit = min(a.M, (int)(blockIdx.y + 1) * a.rows_per_group);
   const int wrow0 = blockIdx.y * a.rows_per_group + wave * 32 * QB;  // first row of this wave
@@ -186,14 +186,23 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
   int seg_lo = -1, seg_hi = -1;  // (sequence, KV head) segments this workgroup holds tiles of
   while (true) {
     const int b = sw.b, g = sw.g;
-    if (seg_lo < 0) seg_lo = b * a.Hkv + g;
-    seg_hi = b * a.Hkv + g;
     const unsigned s_first = sw.seq_first + (unsigned)(g * sw.nt);
     const int tile0 = (int)(x - s_first);
     const unsigned piece_end = min(x_end, s_first + (unsigned)sw.nt);
-    const int n = (int)(piece_end - x);  // tiles of this piece
+    const int n_prefix = sw.nt - a.tree_tiles * a.tree_weight;  // tiles of cached KV; the tree tiles (if any) follow
+    // Real tiles of this piece (the segment's empty tiles after its tree tiles
+    // only weigh the split); a piece of empty tiles alone is skipped.
+    const unsigned real_end = s_first + (unsigned)(n_prefix + a.tree_tiles);
+    const int n = x < real_end ? (int)(min(piece_end, real_end) - x) : 0;
+    if (n <= 0) {
+      x = piece_end;
+      if (x >= x_end) break;
+      if (!walk_next(&sw, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles, a.tree_weight)) break;
+      continue;
+    }
+    if (seg_lo < 0) seg_lo = b * a.Hkv + g;
+    seg_hi = b * a.Hkv + g;
     const int L = valid_prefix(a.prefix_len, b, a.Lcap);
-    const int n_prefix = sw.nt - a.tree_tiles;  // tiles of cached KV; the tree tiles (if any) follow
     const bool has_tree = a.tree_tiles && tile0 + n > n_prefix;
     const int slot = w + b * a.Hkv + g;
     const size_t kv_off = (size_t)(b * a.Hkv + g) * (size_t)a.Lcap * D;
@@ -766,7 +775,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
 
     x = piece_end;
     if (x >= x_end) break;
-    if (!walk_next(&sw, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles)) break;
+    if (!walk_next(&sw, a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles, a.tree_weight)) break;
     __syncthreads();  // staging area, anc_s / bad_s of this piece are no longer read
   }
 
@@ -779,7 +788,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
   // bound the share's rows come out NaN with HTA_STATUS_MERGE_TIMEOUT -- and
   // merges its rows (merge_row.h) from all contributors' slots. The last
   // contributor past the wait clears the segment's words for the next launch.
-  if (a.fuse) {
+  if (a.fuse && seg_lo >= 0) {  // (a workgroup holding only empty tiles contributes to no segment)
     constexpr int kSpinLimit = 1 << 15;  // about 40 ms of polling
     const int RG = (int)gridDim.y;
     // The partials went out as device-coherent (write-through) stores: once
@@ -799,7 +808,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
       const int b = sg / a.Hkv, g = sg % a.Hkv;
       unsigned first;
       int count;
-      segment_tiles(a.prefix_len, a.Hkv, a.Lcap, NK, a.tree_tiles, b, g, &first, &count);
+      segment_tiles(a.prefix_len, a.Hkv, a.Lcap, NK, a.tree_tiles, b, g, &first, &count, a.tree_weight);
       const unsigned w_first = split_owner(first, (unsigned)a.nwg, TT);
       const unsigned w_last = split_owner(first + (unsigned)count - 1, (unsigned)a.nwg, TT);
       const int n_range = (int)(w_last - w_first) + 1;  // slots of the segment (some empty when TT < nwg)
@@ -952,6 +961,7 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
   a.nwg = pl.nwg;
   a.rows_per_group = pl.rows_per_group;
   a.tree_tiles = in.k_tree ? tree_tiles_for(d.T, mfma::NK) : 0;
+  a.tree_weight = in.k_tree ? kTreeTileWeight : 1;
   a.scale_log2 = d.scale_log2;
   a.fuse = fuse.out != nullptr && in.k_tree != nullptr;
   a.out = fuse.out;

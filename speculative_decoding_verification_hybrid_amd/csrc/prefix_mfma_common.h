@@ -28,7 +28,7 @@ struct PrefixArgs {
   int* err_b;
   int* status;
   int B, Hq, Hkv, G, T, Lcap, M;
-  int nwg, rows_per_group, tree_tiles;
+  int nwg, rows_per_group, tree_tiles, tree_weight;
   float scale_log2;
   // Fused merge (fuse != 0): final out (bf16) and lse, and per (segment, row
   // group) words: seg_sync[2 i] arrivals and seg_sync[2 i + 1] departures
