@@ -44,7 +44,8 @@ constexpr int kMaxKeyLoads = (kArgmaxMaxSplit + 3) / 4;  // per thread of the wa
 // Order-preserving map of a float's bits to an unsigned int (larger float,
 // larger key); NaN inputs are not ordered meaningfully.
 __device__ __forceinline__ unsigned ordered_bits(float x) {
-  const unsigned u = __float_as_uint(x);
+  unsigned u = __float_as_uint(x);
+  u = u == 0x80000000u ? 0u : u;  // -0 and +0 compare equal, so they share a key
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -253,7 +254,9 @@ __global__ void __launch_bounds__(256) commit_kernel(const void* k_tree, const v
     const unsigned old = atomicAdd(&count[b], 1u);
     if (old == 2u * (unsigned)Hkv - 1u) {  // the sequence's last workgroup
       count[b] = 0;
-      if (n > 0) {
+      if (L < 0 || L > Lcap)
+        atomicOr(status, kStatusBadPrefix);  // no cache length to append to
+      else if (n > 0) {
         if (fits)
           prefix_len[b] = L + n;
         else

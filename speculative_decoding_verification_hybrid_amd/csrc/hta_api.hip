@@ -77,8 +77,8 @@ int validate(const hta_config_t* c) {
 // whenever there are two blocks or more, so every K / V fragment read from LDS
 // feeds two MFMAs; qb = 1 is taken on request or for a single block, and at
 // D = 128 it may use up to 8 waves (two per SIMD, accumulators in VGPRs).
-// VALU path: 16 rows per workgroup. DOT path: all M rows in one workgroup of
-// 4 waves.
+// VALU path: 16 rows per workgroup. DOT path: up to 8 rows per workgroup of
+// 4 waves (two row groups above 8 rows).
 void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) {
   pl->path = path;
   if (path == HTA_PATH_MFMA) {
@@ -97,8 +97,8 @@ void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) 
     pl->qb = qb;
   } else if (path == HTA_PATH_DOT) {
     pl->tile_tokens = hta::kTileTokens;
-    pl->row_groups = 1;
-    pl->rows_per_group = d.M;
+    pl->row_groups = hta::dot_row_groups(d.M);
+    pl->rows_per_group = d.M > 8 ? 8 : d.M;
     pl->waves = 4;
     pl->qb = 0;
   } else {

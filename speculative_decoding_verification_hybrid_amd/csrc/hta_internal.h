@@ -75,11 +75,13 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
 hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                               int* err_b, int* status, hipStream_t s);
 // Small-M bf16 split-KV kernel (v_dot2 + DPP; D = 128, at most kDotMaxRows
-// query rows per KV head). Float slots, same split and tree fusion.
-constexpr int kDotMaxRows = 8;
+// query rows per KV head, in dot_row_groups(M) groups of up to 8 on grid.y).
+// Float slots, same split and tree fusion.
+constexpr int kDotMaxRows = 16;
 hipError_t launch_prefix_dot(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                              int* err_b, int* status, hipStream_t s);
 bool prefix_dot_supported(int D, int M, bool bf16);
+int dot_row_groups(int M);
 int prefix_dot_occupancy(int M);
 // The drafter's sliding-window self-attention over a ring of W = Lcap slots
 // with T new tokens (window.hip), and the append of the new tokens to the

@@ -1,12 +1,14 @@
 // Split-KV attention for bf16 layers with few query rows per KV head
-// (M = G*T <= 8): the drafter's cross-attention over the target's KV cache
+// (M = G*T <= 16): the drafter's cross-attention over the target's KV cache
 // (LongSpec summary pages, §2.A "memory-efficient architecture": the draft
 // model reads the target model's cache instead of keeping its own), and
 // verification of very small trees. With so few rows a 32-row MFMA block would
 // be mostly padding, so scores and outputs are formed with v_dot2_f32_bf16 on
 // the vector ALUs and reduced across lanes with DPP. Same work split,
 // fused tree tile and partial-result slots (float) as the other split-KV
-// kernels (common.h).
+// kernels (common.h). Above 8 rows the rows are split into two groups of up
+// to 8 (grid.y); the two workgroups of one range run side by side on one XCD,
+// so the second reads the keys and values from its L2.
 //
 // Layout of one wave (64 lanes = 4 groups of 16): lane (grp, c) loads the 16
 // bytes at dims 8c..8c+7 of one token per load, so a single 16-byte load of
@@ -126,6 +128,7 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
   const int grp = lane >> 4, c = lane & 15;
   const int slot_own = c >> 1;     // token slot of this lane's scores
   const int rbase = (c & 1) * NV;  // first row of this lane's scores
+  const int r0 = (int)blockIdx.y * MR;  // this workgroup's first row
 
   const int w = xcd_remap(blockIdx.x, a.nwg);
   const unsigned TT = total_tiles(a.prefix_len, a.B, a.Hkv, a.Lcap, NK, a.tree_tiles);
@@ -163,16 +166,17 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       __syncthreads();
     }
 
-    // query rows of this KV head, dims 8c..8c+7 (rows past M are zero)
+    // this group's query rows of the KV head, dims 8c..8c+7 (rows past M are zero)
     u32x4 qr[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
-      qr[r] = r < a.M ? *(const u32x4*)(qp + (size_t)r * D + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      qr[r] = r0 + r < a.M ? *(const u32x4*)(qp + (size_t)(r0 + r) * D + 8 * c) : u32x4{0u, 0u, 0u, 0u};
 
     // ancestor word of the tree node behind each of this lane's rows
     unsigned long long vis_row[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) vis_row[j] = (has_tree && rbase + j < a.M) ? anc_s[(rbase + j) % a.T] : 0ull;
+    for (int j = 0; j < NV; ++j)
+      vis_row[j] = (has_tree && r0 + rbase + j < a.M) ? anc_s[(r0 + rbase + j) % a.T] : 0ull;
 
     float o[MR][8];
 #pragma unroll
@@ -243,7 +247,7 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       float s[NV], um[NV];
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const bool seen = rbase + j < a.M && tk < nvalid && (!tree || ((vis_row[j] >> tk) & 1ull));
+        const bool seen = r0 + rbase + j < a.M && tk < nvalid && (!tree || ((vis_row[j] >> tk) & 1ull));
         s[j] = seen ? xs[j] * a.scale_log2 : -__builtin_inff();
         float v = s[j];
         v = fmaxf(v, dpp<kRor4>(v));
@@ -352,7 +356,7 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
     __syncthreads();
     for (int idx = tid; idx < MR * D; idx += 256) {
       const int r = idx / D, d = idx % D;
-      if (r >= a.M) continue;
+      if (r0 + r >= a.M) continue;
       float ms = -__builtin_inff();
 #pragma unroll
       for (int q = 0; q < NWAVE; ++q) ms = fmaxf(ms, red_m[q][r]);
@@ -363,8 +367,8 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
         lt += f * red_l[q][r];
         ot += f * red_o[q][r][d];
       }
-      a.slot_o[((size_t)slot * a.M + r) * D + d] = lt > 0.f ? ot / lt : 0.f;
-      if (d == 0) a.slot_lse2[(size_t)slot * a.M + r] = lt > 0.f ? ms + fast_log2(lt) : -__builtin_inff();
+      a.slot_o[((size_t)slot * a.M + r0 + r) * D + d] = lt > 0.f ? ot / lt : 0.f;
+      if (d == 0) a.slot_lse2[(size_t)slot * a.M + r0 + r] = lt > 0.f ? ms + fast_log2(lt) : -__builtin_inff();
     }
     if (has_tree && g == 0 && tid == 0) {
       a.err_b[b] = bad_s;
@@ -379,16 +383,19 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
 
 typedef void (*KernelFn)(DotArgs);
 
+// Rows per workgroup for M rows in all (two groups of up to 8 above 8 rows).
 KernelFn pick(int M) {
   if (M <= 2) return prefix_dot_kernel<2>;
   if (M <= 4) return prefix_dot_kernel<4>;
-  if (M <= 8) return prefix_dot_kernel<8>;
+  if (M <= kDotMaxRows) return prefix_dot_kernel<8>;
   return nullptr;
 }
 
 }  // namespace
 
 bool prefix_dot_supported(int D_, int M, bool bf16) { return bf16 && D_ == D && M >= 1 && M <= kDotMaxRows; }
+
+int dot_row_groups(int M) { return M > 8 ? 2 : 1; }
 
 int prefix_dot_occupancy(int M) {
   KernelFn k = pick(M);
@@ -403,7 +410,7 @@ int prefix_dot_occupancy(int M) {
 hipError_t launch_prefix_dot(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                              int* err_b, int* status, hipStream_t s) {
   KernelFn k = pick(d.M);
-  if (!k || d.D != D || !d.bf16) return hipErrorInvalidValue;
+  if (!k || d.D != D || !d.bf16 || pl.row_groups != dot_row_groups(d.M)) return hipErrorInvalidValue;
   DotArgs a;
   a.q = in.q;
   a.k = in.k_cache;
@@ -426,7 +433,7 @@ hipError_t launch_prefix_dot(const Dims& d, const PrefixLaunch& pl, const Prefix
   a.nwg = pl.nwg;
   a.tree_tiles = in.k_tree ? 1 : 0;
   a.scale_log2 = d.scale_log2;
-  hipLaunchKernelGGL(k, dim3(pl.nwg, 1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k, dim3(pl.nwg, pl.row_groups), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

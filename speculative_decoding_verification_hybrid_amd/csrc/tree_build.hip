@@ -40,7 +40,8 @@ constexpr int kTopChunk = kTopThreads * kTopEPT;     // vocabulary entries per w
 constexpr int kScanChunk = 2048;                     // gram end positions per scan workgroup
 
 __device__ __forceinline__ unsigned ordered_bits(float x) {
-  const unsigned u = __float_as_uint(x);
+  unsigned u = __float_as_uint(x);
+  u = u == 0x80000000u ? 0u : u;  // -0 and +0 compare equal, so they share a key
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ unsigned long long make_key(float x, unsigned idx) {
@@ -95,6 +96,7 @@ __device__ void select_top_wave(const unsigned long long* mine, int kk, unsigned
 // with bit 28 set (0 = no key), so its order is that of make_key on the same
 // entries and the first selection runs on 32-bit compares and exchanges.
 __device__ __forceinline__ unsigned ordered16(unsigned bits16) {
+  bits16 = bits16 == 0x8000u ? 0u : bits16;  // -0 ranks as +0
   return (bits16 & 0x8000u) ? (~bits16 & 0xffffu) : (bits16 | 0x8000u);
 }
 __device__ __forceinline__ unsigned slice_key(unsigned bits16, int local) {

@@ -64,8 +64,10 @@ def test_named_workloads_validate(lib, key):
     (dict(tree_nodes=65), hta.HTA_ERR_UNSUPPORTED),
     (dict(num_workgroups=-1), hta.HTA_ERR_INVALID_ARG),
     (dict(force_path=4), hta.HTA_ERR_INVALID_ARG),
-    (dict(force_path=hta.HTA_PATH_DOT), hta.HTA_ERR_UNSUPPORTED),                    # 4 x 64 rows > 8
+    (dict(force_path=hta.HTA_PATH_DOT), hta.HTA_ERR_UNSUPPORTED),                    # 4 x 64 rows > 16
     (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2), hta.HTA_OK),                  # 4 x 2 rows
+    (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=4), hta.HTA_OK),                  # 4 x 4 rows
+    (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=5), hta.HTA_ERR_UNSUPPORTED),     # 4 x 5 rows > 16
     (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2, dtype="f32"), hta.HTA_ERR_UNSUPPORTED),
     (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2, head_dim=64), hta.HTA_ERR_UNSUPPORTED),
     (dict(force_path=hta.HTA_PATH_MFMA, dtype="f32"), hta.HTA_ERR_UNSUPPORTED),

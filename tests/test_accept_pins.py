@@ -182,3 +182,9 @@ def test_commit_appends_path_rows_and_advances_length():
     assert np.array_equal(rows(kc2)[~touched], rows(kc)[~touched])
     assert np.array_equal(rows(vc2)[~touched], rows(vc)[~touched])
     assert L[1] == 17  # inputs untouched
+
+
+def test_signed_zeros_rank_equal():
+    # -0 and +0 are equal values: the lower index wins whichever sign it has
+    assert oracle.target_tokens(np.array([[-1.0, -0.0, 0.0, -2.0]]))[0] == 1
+    assert oracle.target_tokens(np.array([[-1.0, 0.0, -0.0, -2.0]]))[0] == 1

@@ -40,6 +40,9 @@ CROSS = {
     "m3_ragged": dict(B=6, Hq=6, Hkv=2, D=128, Lcap=1000, T=1, prefix_len=[1, 63, 64, 65, 1000, 0]),
     "qwq_gqa5_t1": dict(B=4, Hq=40, Hkv=8, D=128, Lcap=2000, T=1, prefix_len=[2000, 1, 64, 1500]),  # M = 5
     "gqa4_t2_m8": dict(B=2, Hq=16, Hkv=4, D=128, Lcap=900, T=2, prefix_len=[900, 65]),        # M = 8
+    "gqa4_t3_m12": dict(B=2, Hq=16, Hkv=4, D=128, Lcap=1200, T=3, prefix_len=[1200, 97]),     # M = 12: 2 groups
+    "gqa5_t3_m15": dict(B=1, Hq=40, Hkv=8, D=128, Lcap=700, T=3, prefix_len=[700]),          # M = 15
+    "mha_t9_ragged": dict(B=3, Hq=2, Hkv=2, D=128, Lcap=300, T=9, prefix_len=[300, 1, 65]),  # M = 9
     "poison_tail": dict(B=3, Hq=8, Hkv=2, D=128, Lcap=500, T=1, prefix_len=[77, 500, 1], poison_tail=True),
     "unit_tails": dict(B=5, Hq=8, Hkv=2, D=128, Lcap=200, T=1, prefix_len=[31, 32, 33, 95, 97]),
     "drift_keys": dict(B=1, Hq=32, Hkv=8, D=128, Lcap=5000, T=1, prefix_len=[5000], drift=True),
@@ -104,6 +107,11 @@ SMALL_TREES = {
     "t8_mha": dict(B=2, Hq=4, Hkv=4, D=128, Lcap=500, T=8, prefix_len=[500, 0]),
     "t5_chain_mha": dict(B=1, Hq=2, Hkv=2, D=128, Lcap=300, T=5, prefix_len=[257], parents=[tree_chain(5)]),
     "t4_gqa2_forest": dict(B=1, Hq=4, Hkv=2, D=128, Lcap=128, T=4, prefix_len=[128], parents=[[-1, 0, -1, 2]]),
+    "t9_mha": dict(B=2, Hq=2, Hkv=2, D=128, Lcap=700, T=9, prefix_len=[700, 65]),
+    "t3_gqa4_m12": dict(B=2, Hq=8, Hkv=2, D=128, Lcap=1000, T=3, prefix_len=[1000, 64]),
+    "t5_gqa3_m15_chain": dict(B=1, Hq=6, Hkv=2, D=128, Lcap=400, T=5, prefix_len=[399], parents=[tree_chain(5)]),
+    "t7_gqa2_m14_forest": dict(B=1, Hq=4, Hkv=2, D=128, Lcap=256, T=7, prefix_len=[130],
+                               parents=[[-1, 0, -1, 2, 1, 3, -1]]),
 }
 
 

@@ -11,7 +11,7 @@ import torch
 import oracle
 from gpu_util import say
 from speculative_decoding_verification_hybrid_amd import hta
-from workloads import make_tree_case
+from workloads import f32_to_bf16_bits, make_tree_case
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +92,19 @@ def test_bad_history_len_gives_empty_tree_and_status():
     rt, rp, rn = oracle.build_trees(case.history[:1], case.history_len[:1], case.logits_f64()[:1], 3, 2, 2,
                                     [2, 2, 2], 8)
     assert np.array_equal(tok[:1], rt) and np.array_equal(par[:1], rp) and nn[0] == rn[0]
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 5000), ("f32", 257)])
+def test_signed_zero_ties(dtype, V):
+    # the largest logits are zeros of both signs: they rank as equals, by index
+    case = make_tree_case(B=2, V=V, cap=800, history_len=[800, 300], alphabet=6, dtype="f32", seed=41)
+    rng = np.random.default_rng(42)
+    lg = -1.0 - np.abs(case.logits.astype(np.float64))
+    for b in range(case.B):
+        pos = rng.choice(V, size=10, replace=False)
+        lg[b, pos] = np.where(np.arange(10) % 2 == 0, -0.0, 0.0)
+    case.logits = lg.astype(np.float32)
+    if dtype == "bf16":
+        case.logits = f32_to_bf16_bits(case.logits)
+        case.dtype = "bf16"
+    _check(case, 8, 2, 6, [4, 3, 2, 2, 1, 1, 1, 1], 64)

@@ -16,6 +16,7 @@ import oracle
 from oracle import tree_oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tree_hand_example.json")
+GOLDEN_M2 = os.path.join(os.path.dirname(__file__), "golden", "tree_hand_example_m2.json")
 
 
 def _loop_ranking(v, n):
@@ -58,14 +59,17 @@ def test_most_recent_match_matches_forward_scan(seed):
 
 
 def _golden_inputs(g):
+    if "logits" in g:
+        return g["history"], np.array(g["logits"], dtype=np.float64)
     logits = np.zeros(g["vocab"])
     for t, val in g["logits_nonzero"].items():
         logits[int(t)] = val
     return g["history"], logits
 
 
-def test_hand_example():
-    g = json.load(open(GOLDEN))
+@pytest.mark.parametrize("path", [GOLDEN, GOLDEN_M2])
+def test_hand_example(path):
+    g = json.load(open(path))
     hist, logits = _golden_inputs(g)
     tok, par, n = oracle.build_tree(hist, logits, g["k"], g["m"], g["keep_first"], g["keep"], g["T"])
     assert list(tok) == g["tokens"] and list(par) == g["parent"] and n == g["n_nodes"]
@@ -116,3 +120,26 @@ def test_structure_and_truncation(seed):
         t2, p2, n2 = oracle.build_tree(hist, logits, k, m, kf, keep, T)
         assert list(t2[:min(T, n)]) == list(tok[:min(T, n)]) and n2 == min(T, n)
         assert list(p2[:n2]) == list(par[:n2])
+
+
+def test_signed_zeros_rank_equal():
+    # -0 and +0 tie, so they rank by index like any other tie
+    v = np.array([-1.0, -0.0, 0.0, -0.0, -3.0])
+    assert oracle.ranked_tokens(v, 4) == [1, 2, 3, 0]
+
+
+def test_planted_mistakes_fail_the_bigram_example(monkeypatch):
+    g = json.load(open(GOLDEN_M2))
+    hist, logits = _golden_inputs(g)
+    args = (hist, logits, g["k"], g["m"], g["keep_first"], g["keep"], g["T"])
+    good = tree_oracle.build_tree(*args)
+    # (1) ties ranked by higher index first
+    monkeypatch.setattr(tree_oracle, "ranked_tokens",
+                        lambda v, n: [int(t) for t in np.lexsort((-np.arange(len(v)), -np.asarray(v)))[:n]])
+    assert list(tree_oracle.build_tree(*args)[0]) != list(good[0])
+    monkeypatch.undo()
+    # (2) query 1 searched up to the last position (x_{i+1}'s own n-gram counts as a match)
+    real = tree_oracle.most_recent_match
+    monkeypatch.setattr(tree_oracle, "most_recent_match",
+                        lambda s, gr, before: real(s, gr, len(s)) if gr == s[len(s) - len(gr):] else real(s, gr, before))
+    assert list(tree_oracle.build_tree(*args)[0]) != list(good[0])
