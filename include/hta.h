@@ -80,7 +80,8 @@ enum hta_status_code {
   HTA_ERR_HIP = -4,         /* a HIP runtime call or kernel enqueue failed */
   HTA_ERR_BAD_TREE = -5,    /* reported through hta_get_status only */
   HTA_ERR_BAD_PREFIX = -6,  /* reported through hta_get_status only */
-  HTA_ERR_NO_DEVICE = -7    /* no usable GPU */
+  HTA_ERR_NO_DEVICE = -7,   /* no usable GPU */
+  HTA_ERR_TOO_LARGE = -8    /* hta_verify_attn_noalloc: shape needs more than its scratch memory */
 };
 
 enum hta_dtype { HTA_F32 = 0, HTA_BF16 = 1 };
@@ -321,6 +322,29 @@ HTA_API int hta_commit(hta_handle_t h, const void* k_tree, const void* v_tree, c
 /* Synchronises `stream`, returns in *device_status the OR of the status
  * bits raised since the last call (HTA_STATUS_*), and clears them. */
 HTA_API int hta_get_status(hta_handle_t h, void* stream, int32_t* device_status);
+
+/* Bytes of device memory that hta_verify_attn_noalloc holds per GPU. */
+#define HTA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and launch plan as hta_verify_attn on a handle made
+ * from *cfg (fuse_merge is ignored: the merge runs as its own launch), with
+ * no handle and no allocation. The partial results live in a fixed device
+ * array of HTA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
+ * from the first call on that GPU until the process ends. A shape whose
+ * partial results need more returns HTA_ERR_TOO_LARGE (a smaller
+ * num_workgroups in *cfg needs less). Calls on one GPU share that array:
+ * calls that overlap on one GPU (other streams, other threads) race, so the
+ * caller orders them. Tensor arguments, layouts and alignment as for
+ * hta_verify_attn, on the current device. status (int32, device) receives
+ * the HTA_STATUS_* bits of this call OR-ed into it; the caller clears it.
+ * Returns HTA_OK, HTA_ERR_INVALID_ARG, HTA_ERR_UNSUPPORTED,
+ * HTA_ERR_TOO_LARGE, HTA_ERR_NO_DEVICE or HTA_ERR_HIP. */
+HTA_API int hta_verify_attn_noalloc(const hta_config_t* cfg, const void* q, const void* k_cache,
+                                    const void* v_cache, const void* k_tree, const void* v_tree,
+                                    const int32_t* parent, const int32_t* prefix_len, void* out, float* lse,
+                                    int32_t* status, void* stream);
 
 /* Static English text for a return code. Never NULL. */
 HTA_API const char* hta_status_string(int status);

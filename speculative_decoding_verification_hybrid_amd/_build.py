@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhta.so")
 SOURCES = ["hta_api.hip", "prefix_mfma.hip", "prefix_valu.hip", "tree.hip", "merge.hip",
            "accept.hip", "prefix_dot.hip",
-           "window.hip", "tree_build.hip"]
+           "window.hip", "tree_build.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 instructions (the host

@@ -118,12 +118,63 @@ void plan_rows(const hta::Dims& d, int path, int qb_req, hta::PrefixLaunch* pl) 
 
 }  // namespace
 
+namespace hta {
+
+int plan_launch(const hta_config_t* cfg, int cus, Dims* dp, PrefixLaunch* pl, int* occ_out) {
+  Dims& d = *dp;
+  d.B = cfg->batch;
+  d.Hq = cfg->n_q_heads;
+  d.Hkv = cfg->n_kv_heads;
+  d.G = d.Hq / d.Hkv;
+  d.T = cfg->tree_nodes;
+  d.D = cfg->head_dim;
+  d.Lcap = cfg->kv_capacity;
+  d.M = d.G * d.T;
+  d.bf16 = cfg->dtype == HTA_BF16;
+  const float scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)d.D);
+  d.scale_log2 = scale * kLog2e;
+
+  int path = cfg->force_path;
+  if (path == HTA_PATH_AUTO)
+    path = (d.bf16 && d.M >= 16)                    ? HTA_PATH_MFMA
+           : prefix_dot_supported(d.D, d.M, d.bf16) ? HTA_PATH_DOT
+                                                    : HTA_PATH_VALU;
+  plan_rows(d, path, cfg->qblocks_per_wave, pl);
+  if (path == HTA_PATH_MFMA && !prefix_mfma_supported(d.D, pl->waves, pl->qb)) return HTA_ERR_UNSUPPORTED;
+  const int occ = path == HTA_PATH_MFMA  ? prefix_mfma_occupancy(d.D, pl->waves, pl->qb)
+                  : path == HTA_PATH_DOT ? prefix_dot_occupancy(d.M)
+                                         : prefix_valu_occupancy(d.D, d.bf16);
+  int64_t nwg = cfg->num_workgroups;
+  if (nwg <= 0) {
+    nwg = (int64_t)cus * (occ > 0 ? occ : 1) / pl->row_groups;
+    nwg = nwg < 8 ? 8 : (nwg / 8) * 8;
+  }
+  // The kernels split tiles with 32-bit arithmetic: keep max_tiles * nwg < 2^32.
+  const int nk = pl->tile_tokens;
+  const int64_t max_tiles = (int64_t)d.B * d.Hkv *
+                            ((d.Lcap + nk - 1) / nk +
+                             tree_tiles_for(d.T, nk) * (path == HTA_PATH_MFMA ? kTreeTileWeight : 1));
+  if (cfg->num_workgroups <= 0 && nwg > max_tiles) nwg = max_tiles;
+  const int64_t nwg_cap = (int64_t)UINT32_MAX / max_tiles;
+  if (nwg_cap < 1) return HTA_ERR_UNSUPPORTED;
+  if (nwg > nwg_cap) nwg = nwg_cap;
+  if (nwg > (1 << 20)) nwg = 1 << 20;
+  pl->nwg = (int)nwg;
+  *occ_out = occ;
+  return HTA_OK;
+}
+
+int launch_split(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots, int* err_b,
+                 int* status, hipStream_t s) {
+  if (pl.path == HTA_PATH_MFMA) return check_hip(launch_prefix_mfma(d, pl, in, slots, err_b, status, s));
+  if (pl.path == HTA_PATH_DOT) return check_hip(launch_prefix_dot(d, pl, in, slots, err_b, status, s));
+  return check_hip(launch_prefix_valu(d, pl, in, slots, err_b, status, s));
+}
+
+}  // namespace hta
+
 static int launch_split(hta_handle_t h, const hta::PrefixInputs& in, hipStream_t s) {
-  if (h->pl.path == HTA_PATH_MFMA)
-    return check_hip(hta::launch_prefix_mfma(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
-  if (h->pl.path == HTA_PATH_DOT)
-    return check_hip(hta::launch_prefix_dot(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
-  return check_hip(hta::launch_prefix_valu(h->dims, h->pl, in, h->slots, h->err_b, h->status, s));
+  return hta::launch_split(h->dims, h->pl, in, h->slots, h->err_b, h->status, s);
 }
 
 extern "C" {
@@ -140,6 +191,7 @@ const char* hta_status_string(int status) {
     case HTA_ERR_BAD_TREE: return "parent array breaks -1 <= parent[i] < i";
     case HTA_ERR_BAD_PREFIX: return "prefix_len outside [0, kv_capacity]";
     case HTA_ERR_NO_DEVICE: return "no usable GPU";
+    case HTA_ERR_TOO_LARGE: return "shape needs more than the no-allocation entry point's scratch memory";
     default: return "unknown status";
   }
 }
@@ -158,51 +210,14 @@ int hta_create(hta_handle_t* out, const hta_config_t* cfg) {
   if (!h) return HTA_ERR_NO_MEMORY;
   h->cfg = *cfg;
   hta::Dims& d = h->dims;
-  d.B = cfg->batch;
-  d.Hq = cfg->n_q_heads;
-  d.Hkv = cfg->n_kv_heads;
-  d.G = d.Hq / d.Hkv;
-  d.T = cfg->tree_nodes;
-  d.D = cfg->head_dim;
-  d.Lcap = cfg->kv_capacity;
-  d.M = d.G * d.T;
-  d.bf16 = cfg->dtype == HTA_BF16;
-  const float scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)d.D);
-  d.scale_log2 = scale * hta::kLog2e;
-
-  int path = cfg->force_path;
-  if (path == HTA_PATH_AUTO)
-    path = (d.bf16 && d.M >= 16)                         ? HTA_PATH_MFMA
-           : hta::prefix_dot_supported(d.D, d.M, d.bf16) ? HTA_PATH_DOT
-                                                         : HTA_PATH_VALU;
-  plan_rows(d, path, cfg->qblocks_per_wave, &h->pl);
-  if (path == HTA_PATH_MFMA && !hta::prefix_mfma_supported(d.D, h->pl.waves, h->pl.qb)) {
+  int occ = 0;
+  const int rc = hta::plan_launch(cfg, cus, &d, &h->pl, &occ);
+  if (rc != HTA_OK) {
     delete h;
-    return HTA_ERR_UNSUPPORTED;
+    return rc;
   }
-  const int occ = path == HTA_PATH_MFMA  ? hta::prefix_mfma_occupancy(d.D, h->pl.waves, h->pl.qb)
-                  : path == HTA_PATH_DOT ? hta::prefix_dot_occupancy(d.M)
-                                         : hta::prefix_valu_occupancy(d.D, d.bf16);
-  int64_t nwg = cfg->num_workgroups;
-  if (nwg <= 0) {
-    nwg = (int64_t)cus * (occ > 0 ? occ : 1) / h->pl.row_groups;
-    nwg = nwg < 8 ? 8 : (nwg / 8) * 8;
-  }
-  // The kernels split tiles with 32-bit arithmetic: keep max_tiles * nwg < 2^32.
-  const int nk = h->pl.tile_tokens;
-  const int64_t max_tiles = (int64_t)d.B * d.Hkv *
-                            ((d.Lcap + nk - 1) / nk + hta::tree_tiles_for(d.T, nk) *
-                                                          (path == HTA_PATH_MFMA ? hta::kTreeTileWeight : 1));
-  if (cfg->num_workgroups <= 0 && nwg > max_tiles) nwg = max_tiles;
-  const int64_t nwg_cap = (int64_t)UINT32_MAX / max_tiles;
-  if (nwg_cap < 1) {
-    delete h;
-    return HTA_ERR_UNSUPPORTED;
-  }
-  if (nwg > nwg_cap) nwg = nwg_cap;
-  if (nwg > (1 << 20)) nwg = 1 << 20;
-  h->pl.nwg = (int)nwg;
-
+  const int path = h->pl.path;
+  const int64_t nwg = h->pl.nwg;
   const int64_t max_slots = nwg + (int64_t)d.B * d.Hkv - 1;
   size_t off = 0;
   const size_t off_so = off;

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "hta.h"
+
 namespace hta {
 
 constexpr int kTileTokens = 64;      // prefix tokens per tile of the split (VALU and DOT paths)
@@ -74,6 +76,13 @@ hipError_t launch_prefix_mfma(const Dims& d, const PrefixLaunch& pl, const Prefi
                               int* err_b, int* status, hipStream_t s, const FusedMerge& fuse = FusedMerge());
 hipError_t launch_prefix_valu(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                               int* err_b, int* status, hipStream_t s);
+// Launch plan of a validated config on a device with `cus` compute units: the
+// dims, the kernel path, rows, waves and workgroup count, and the chosen
+// kernel's workgroups per CU. Allocates nothing. Returns HTA_OK or an HTA_ERR_*.
+int plan_launch(const hta_config_t* cfg, int cus, Dims* d, PrefixLaunch* pl, int* occ);
+// The planned split-KV launch (any path) into `slots`; HTA_OK or HTA_ERR_HIP.
+int launch_split(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots, int* err_b,
+                 int* status, hipStream_t s);
 // Small-M bf16 split-KV kernel (v_dot2 + DPP; D = 128, at most kDotMaxRows
 // query rows per KV head, in dot_row_groups(M) groups of up to 8 on grid.y).
 // Float slots, same split and tree fusion.

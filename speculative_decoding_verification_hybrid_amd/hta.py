@@ -28,6 +28,8 @@ HTA_ERR_HIP = -4
 HTA_ERR_BAD_TREE = -5
 HTA_ERR_BAD_PREFIX = -6
 HTA_ERR_NO_DEVICE = -7
+HTA_ERR_TOO_LARGE = -8
+HTA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 HTA_F32 = 0
 HTA_BF16 = 1
@@ -126,6 +128,7 @@ _SIGNATURES = {
     "hta_commit": (ctypes.c_int, [_vp] * 8 + [_vp]),
     "hta_get_status": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(_i32)]),
     "hta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "hta_verify_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(HtaConfig)] + [_vp] * 10 + [_vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -266,6 +269,28 @@ def hta_verify_attn(h: Handle, q, k_cache, v_cache, k_tree, v_tree, parent, pref
     ]
     _check(load_library().hta_verify_attn(_vp(h.ptr), *[_vp(a) for a in args], _vp(_stream_ptr(stream))),
            "hta_verify_attn")
+
+
+def hta_verify_attn_noalloc(cfg: HtaConfig, q, k_cache, v_cache, k_tree, v_tree, parent, prefix_len, out, lse,
+                            status, stream=None) -> None:
+    """hta_verify_attn without a handle or any allocation; status: int32 [1] on the device."""
+    import torch
+    B, Hq, Hkv, D, T, Lcap = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.tree_nodes, cfg.kv_capacity
+    dt = torch.bfloat16 if cfg.dtype == HTA_BF16 else torch.float32
+    args = [
+        _tensor(q, "q", dt, (B, Hq, T, D)),
+        _tensor(k_cache, "k_cache", dt, (B, Hkv, Lcap, D)),
+        _tensor(v_cache, "v_cache", dt, (B, Hkv, Lcap, D)),
+        _tensor(k_tree, "k_tree", dt, (B, Hkv, T, D)),
+        _tensor(v_tree, "v_tree", dt, (B, Hkv, T, D)),
+        _tensor(parent, "parent", torch.int32, (B, T)),
+        _tensor(prefix_len, "prefix_len", torch.int32, (B,)),
+        _tensor(out, "out", dt, (B, Hq, T, D)),
+        _tensor(lse, "lse", torch.float32, (B, Hq, T)),
+        _tensor(status, "status", torch.int32, (1,)),
+    ]
+    _check(load_library().hta_verify_attn_noalloc(ctypes.byref(cfg), *[_vp(a) for a in args],
+                                                  _vp(_stream_ptr(stream))), "hta_verify_attn_noalloc")
 
 
 def hta_tree_mask(h: Handle, parent, mask_out, stream=None) -> None:
