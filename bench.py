@@ -93,9 +93,29 @@ def algorithmic_bytes(w):
     return kv, kv + tree_kv + q_out + lse + meta
 
 
+def source_hash(src):
+    """sha256 (first 16 hex) of a kernel source and the repository headers it includes, in
+    include order, so a change to any of them marks counter summaries taken before as stale."""
+    h, seen = hashlib.sha256(), set()
+
+    def add(path):
+        if path in seen or not os.path.exists(path):
+            return
+        seen.add(path)
+        text = open(path, "rb").read()
+        h.update(text)
+        for ln in text.decode("utf-8", "replace").splitlines():
+            ln = ln.strip()
+            if ln.startswith('#include "'):
+                add(os.path.join(os.path.dirname(path), ln.split('"')[1]))
+
+    add(src)
+    return h.hexdigest()[:16]
+
+
 def traffic_from_profile(path=TRAFFIC_FILE, src=PREFIX_SRC, key="hbm_bytes_per_launch"):
     """HBM bytes per launch of a kernel from a committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on the current kernel source and headers; else None."""
     if not os.path.exists(path):
         return None
     fields = {}
@@ -103,8 +123,7 @@ def traffic_from_profile(path=TRAFFIC_FILE, src=PREFIX_SRC, key="hbm_bytes_per_l
         if "=" in ln and not ln.startswith("#"):
             k, v = ln.split("=", 1)
             fields[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if fields.get("kernel_source_sha256_16") != src_hash:
+    if fields.get("kernel_source_sha256_16") != source_hash(src):
         return None
     try:
         return float(fields[key])

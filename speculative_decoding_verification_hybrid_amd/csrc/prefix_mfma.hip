@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
   constexpr int NBLK = NK / RPB;           // copies per K (or V) tile
   constexpr int KPW = NBLK / NWAVE;        // K (and V) copies per wave per tile
   constexpr int CPW = 2 * KPW;             // copies per wave per tile
-  constexpr int SROW = D + 8;              // epilogue staging row (16-byte aligned)
+  constexpr int SROW = D;                  // epilogue staging row; 16-byte chunks XOR-swizzled by row
   constexpr int NPV = 2 * DB * QB;         // P.V MFMAs per tile
   constexpr int NSC = KC * QB;             // score MFMAs per tile
   constexpr int NSLOT = NPV + NSC;
@@ -720,8 +720,10 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     __syncthreads();  // every copy has landed and no wave reads the tile buffers any more
 
     // Epilogue: O^T holds dims db*32 + 8*(v/4) + 4*hh + v%4 of row rowq[X].
-    // Normalise, round to bf16 and stage this wave's rows in LDS (rows padded
-    // by 16 bytes), then write them out as whole contiguous rows.
+    // Normalise, round to bf16 and stage this wave's rows in LDS (16-byte
+    // chunk c of row r at chunk c ^ (r mod DCH), so the 32 rows a store
+    // instruction touches spread over the banks), then write them out as
+    // whole contiguous rows.
     unsigned short* stg = lds + wave * 32 * QB * SROW;
 #pragma unroll
     for (int X = 0; X < QB; ++X) {
@@ -737,7 +739,8 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
                   ((unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 1] * inv) << 16);
           pk[1] = (unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 2] * inv) |
                   ((unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 3] * inv) << 16);
-          *(u32x2*)(stg + (32 * X + l32) * SROW + d) = pk;
+          const int r = 32 * X + l32;
+          *(u32x2*)(stg + r * SROW + (((d >> 3) ^ (r & (DCH - 1))) << 3) + (d & 7)) = pk;
         }
       if (okq[X] && hh == 0) {
         const float v = m[X] + fast_log2(lt);
@@ -753,7 +756,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     for (int i = 0; i < 32 * QB * DCH / 64; ++i) {
       const int u = i * 64 + lane;
       const int rr = u / DCH, c = u % DCH;
-      const u32x4 val = *(const u32x4*)(stg + rr * SROW + c * 8);
+      const u32x4 val = *(const u32x4*)(stg + rr * SROW + ((c ^ (rr & (DCH - 1))) << 3));
       if (wrow0 + rr < row_limit) {
         if (a.fuse)
           __builtin_amdgcn_raw_buffer_store_b128(val, slot_rsrc(a.slot_o, a.slot_bytes_o),
@@ -889,27 +892,30 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
 typedef void (*KernelFn)(PrefixArgs);
 
 // Instances: every (QB, waves) the plan can pick -- QB = 2 with 1, 2 or 4
-// waves, QB = 1 (on request, or for a single 32-row block) with 1, 2 or 4 --
-// at D = 128 and 64, each with the stage count that fills the LDS.
+// waves, QB = 1 (on request, or for a single 32-row block) with 1, 2, 4 or 8
+// at D = 128 -- at D = 128 and 64. Four stages: deeper rings (up to 9 at
+// D = 128) measured no faster, since the loop is bound by instruction issue
+// rather than by memory latency, and the smaller ring lets two workgroups
+// share a CU where registers allow.
 struct Inst {
   int D, qb, waves, stages;
   KernelFn fn;
 };
-constexpr int kNsLarge = 9;  // 144 KB of 16 KB stages (D = 128)
+constexpr int kStages = 4;
 const Inst kInst[] = {
-    {128, 1, 8, kNsLarge, prefix_mfma_kernel<128, 1, 8, kNsLarge>},
-    {128, 2, 4, kNsLarge, prefix_mfma_kernel<128, 2, 4, kNsLarge>},
-    {128, 2, 2, kNsLarge, prefix_mfma_kernel<128, 2, 2, kNsLarge>},
-    {128, 2, 1, kNsLarge, prefix_mfma_kernel<128, 2, 1, kNsLarge>},
-    {128, 1, 4, kNsLarge, prefix_mfma_kernel<128, 1, 4, kNsLarge>},
-    {128, 1, 2, kNsLarge, prefix_mfma_kernel<128, 1, 2, kNsLarge>},
-    {128, 1, 1, kNsLarge, prefix_mfma_kernel<128, 1, 1, kNsLarge>},
-    {64, 2, 4, 10, prefix_mfma_kernel<64, 2, 4, 10>},
-    {64, 2, 2, 10, prefix_mfma_kernel<64, 2, 2, 10>},
-    {64, 2, 1, 10, prefix_mfma_kernel<64, 2, 1, 10>},
-    {64, 1, 4, 10, prefix_mfma_kernel<64, 1, 4, 10>},
-    {64, 1, 2, 10, prefix_mfma_kernel<64, 1, 2, 10>},
-    {64, 1, 1, 10, prefix_mfma_kernel<64, 1, 1, 10>},
+    {128, 1, 8, kStages, prefix_mfma_kernel<128, 1, 8, kStages>},
+    {128, 2, 4, kStages, prefix_mfma_kernel<128, 2, 4, kStages>},
+    {128, 2, 2, kStages, prefix_mfma_kernel<128, 2, 2, kStages>},
+    {128, 2, 1, kStages, prefix_mfma_kernel<128, 2, 1, kStages>},
+    {128, 1, 4, kStages, prefix_mfma_kernel<128, 1, 4, kStages>},
+    {128, 1, 2, kStages, prefix_mfma_kernel<128, 1, 2, kStages>},
+    {128, 1, 1, kStages, prefix_mfma_kernel<128, 1, 1, kStages>},
+    {64, 2, 4, kStages, prefix_mfma_kernel<64, 2, 4, kStages>},
+    {64, 2, 2, kStages, prefix_mfma_kernel<64, 2, 2, kStages>},
+    {64, 2, 1, kStages, prefix_mfma_kernel<64, 2, 1, kStages>},
+    {64, 1, 4, kStages, prefix_mfma_kernel<64, 1, 4, kStages>},
+    {64, 1, 2, kStages, prefix_mfma_kernel<64, 1, 2, kStages>},
+    {64, 1, 1, kStages, prefix_mfma_kernel<64, 1, 1, kStages>},
 };
 
 const Inst* find(int D, int qb, int waves) {
