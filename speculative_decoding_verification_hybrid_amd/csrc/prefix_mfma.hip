@@ -762,8 +762,8 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
           __builtin_amdgcn_raw_buffer_store_b128(val, slot_rsrc(a.slot_o, a.slot_bytes_o),
                                                  ((unsigned)(slot * a.M + wrow0 + rr) * D + (unsigned)c * 8) * 2u, 0,
                                                  kCpolDevice);
-        else
-          *(u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8) = val;
+        else  // streamed past the caches: read once, by the merge
+          __builtin_nontemporal_store(val, (u32x4*)(a.slot_o + ((size_t)slot * a.M + wrow0 + rr) * D + c * 8));
       }
     }
     // The workgroup holding the first tree tile of (b, KV head 0) reports the
