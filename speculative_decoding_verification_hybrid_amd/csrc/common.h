@@ -107,6 +107,7 @@ __device__ inline void segment_tiles(const int* prefix_len, int Hkv, int Lcap, i
 // Walks a workgroup's tile range segment by segment.
 struct SegmentWalk {
   int b, g, nt;        // current sequence, KV head, tiles per segment of b
+  int L;               // valid cached length of sequence b
   unsigned seq_first;  // global index of the first tile of sequence b
 };
 
@@ -115,11 +116,13 @@ __device__ inline bool walk_start(SegmentWalk* sw, unsigned x, const int* prefix
                                   int Lcap, int NK, int tree_tiles, int tree_weight = 1) {
   unsigned first = 0;
   for (int b = 0; b < B; ++b) {
-    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles, tree_weight);
+    const int L = valid_prefix(prefix_len, b, Lcap);
+    const int nt = tiles_of(L, NK) + tree_tiles * tree_weight;
     const unsigned span = (unsigned)nt * (unsigned)Hkv;
     if (x < first + span) {
       sw->b = b;
       sw->nt = nt;
+      sw->L = L;
       sw->seq_first = first;
       sw->g = (int)((x - first) / (unsigned)nt);
       return true;
@@ -136,10 +139,12 @@ __device__ inline bool walk_next(SegmentWalk* sw, const int* prefix_len, int B, 
   sw->g = 0;
   sw->seq_first += (unsigned)sw->nt * (unsigned)Hkv;
   for (int b = sw->b + 1; b < B; ++b) {
-    const int nt = seg_tiles(prefix_len, b, Lcap, NK, tree_tiles, tree_weight);
+    const int L = valid_prefix(prefix_len, b, Lcap);
+    const int nt = tiles_of(L, NK) + tree_tiles * tree_weight;
     if (nt > 0) {
       sw->b = b;
       sw->nt = nt;
+      sw->L = L;
       return true;
     }
   }

@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
     const int tile0 = (int)(x - s_first);
     const unsigned piece_end = min(x_end, s_first + (unsigned)sw.nt);
     const int ntiles = (int)(piece_end - x);
-    const int L = valid_prefix(a.prefix_len, b, a.Lcap);
+    const int L = sw.L;
     const int n_prefix = sw.nt - a.tree_tiles;
     const bool has_tree = a.tree_tiles && tile0 + ntiles > n_prefix;
     const int slot = w + b * a.Hkv + g;

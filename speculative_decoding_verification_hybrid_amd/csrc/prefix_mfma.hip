@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     }
     if (seg_lo < 0) seg_lo = b * a.Hkv + g;
     seg_hi = b * a.Hkv + g;
-    const int L = valid_prefix(a.prefix_len, b, a.Lcap);
+    const int L = sw.L;
     const bool has_tree = a.tree_tiles && tile0 + n > n_prefix;
     const int slot = w + b * a.Hkv + g;
     const size_t kv_off = (size_t)(b * a.Hkv + g) * (size_t)a.Lcap * D;
@@ -735,10 +735,8 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + 8 * g4 + 4 * hh;
           u32x2 pk;
-          pk[0] = (unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 0] * inv) |
-                  ((unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 1] * inv) << 16);
-          pk[1] = (unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 2] * inv) |
-                  ((unsigned)float_to_bf16_bits(O[X][db][4 * g4 + 3] * inv) << 16);
+          pk[0] = cvt_pk_bf16(O[X][db][4 * g4 + 0] * inv, O[X][db][4 * g4 + 1] * inv);
+          pk[1] = cvt_pk_bf16(O[X][db][4 * g4 + 2] * inv, O[X][db][4 * g4 + 3] * inv);
           const int r = 32 * X + l32;
           *(u32x2*)(stg + r * SROW + (((d >> 3) ^ (r & (DCH - 1))) << 3) + (d & 7)) = pk;
         }
