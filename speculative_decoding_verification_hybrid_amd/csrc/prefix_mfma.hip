@@ -587,11 +587,14 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
       auto fma_p = [&](int p) __attribute__((always_inline)) {
         xs[p] = fmaf(Sc[p >> 4][p & 15], a.scale_log2, nm[p >> 4]);
       };
+      // (the tie keeps each add in its slot: left alone, the compiler sinks
+      // all of them into one dependent chain after the last slot)
       auto sum_p = [&](int p) __attribute__((always_inline)) {
         if ((p & 15) == 0)
           ps[p >> 4] = pr[p];
         else
           ps[p >> 4] += pr[p];
+        asm volatile("" : "+v"(ps[p >> 4]));
         if (p & 1) pk[p >> 4][(p >> 3) & 1][(p & 7) >> 1] = cvt_pk_bf16(pr[p - 1], pr[p]);
       };
       // The scaled scores run two slots ahead of their exp (a transcendental
