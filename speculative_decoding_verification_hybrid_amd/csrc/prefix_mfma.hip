@@ -525,8 +525,11 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
     // (sum in lsp). Two consecutive tiles swap the roles of the two register
     // sets, so no scores or probabilities are copied between tiles.
     constexpr int TOP = NPV >= 8 ? 2 : 1;  // P.V slots issued ahead of the barrier
-    auto step = [&](const int j, f32x16(&Sc)[QB], f32x16(&Sn)[QB], bf16x8(&Pc)[QB][2], bf16x8(&Pn)[QB][2])
-                    __attribute__((always_inline)) {
+    // A steady step (steady_c true) is one known to take the steady-state
+    // refill below and to need no mask for tile j+1: its code tests neither.
+    auto step = [&](auto steady_c, const int j, f32x16(&Sc)[QB], f32x16(&Sn)[QB], bf16x8(&Pc)[QB][2],
+                    bf16x8(&Pn)[QB][2]) __attribute__((always_inline)) {
+      constexpr bool kSteady = decltype(steady_c)::value;
       if (j > 0) check(j - 1, Pc, lsp, op);
 #pragma unroll
       for (int X = 0; X < QB; ++X)
@@ -549,7 +552,7 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
       // tail) up to two tiles are queued with the general copy.
       auto top = [&]() __attribute__((always_inline)) {
         const int t = j - 2 + NS;
-        if (t < jm && issued == t) {
+        if (kSteady || (t < jm && issued == t)) {
           __builtin_amdgcn_s_waitcnt(vmcnt_only<((NS - 4) * CPW < 63 ? (NS - 4) * CPW : 63)>());
           tile_barrier();
           copy_full(kq, vq, wlds + ocp);
@@ -675,29 +678,48 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
           vf[kc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vh[0][kc][db], vh[1][kc][db], 0, 1, 2, 3, 4,
                                                                            5, 6, 7));
       // Masks of tile j+1 (known now that its scores are).
-      if (j + 1 >= jm && j + 1 < n) mask_scores(Sn, j + 1);
+      if (!kSteady && j + 1 >= jm && j + 1 < n) mask_scores(Sn, j + 1);
       op = oc;
       oc = on;
       on = rot(on);
       ocp = rot(ocp);
     };
     // Tiles in pairs (an odd count starts with a single tile and one copy).
+    // Steps 0 .. n_st-1 are steady: tile j-2+NS is a full prefix tile, queued
+    // in order (the prologue queued NS-2 tiles), so tile j+1 is full too.
+    // The remaining steps take the general path.
     f32x16 S1[QB];
     bf16x8 P1[QB][2];
-    int j = 0;
-    if (n & 1) {
-      step(0, S, S1, P, P1);
+    auto swap_sets = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int X = 0; X < QB; ++X) {
         S[X] = S1[X];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) P[X][kc] = P1[X][kc];
       }
+    };
+    static_assert(P0 == NS - 2, "the steady steps start at tile 0");
+    const int n_st = issued == P0 ? max(0, min(n, jm - P0)) : 0;
+    constexpr std::integral_constant<bool, true> kSteadyStep{};
+    constexpr std::integral_constant<bool, false> kGeneralStep{};
+    int j = 0;
+    if (n_st & 1) {
+      step(kSteadyStep, 0, S, S1, P, P1);
+      swap_sets();
       j = 1;
     }
+    for (; j < n_st; j += 2) {
+      step(kSteadyStep, j, S, S1, P, P1);
+      step(kSteadyStep, j + 1, S1, S, P1, P);
+    }
+    if ((n - j) & 1) {
+      step(kGeneralStep, j, S, S1, P, P1);
+      swap_sets();
+      ++j;
+    }
     for (; j < n; j += 2) {
-      step(j, S, S1, P, P1);
-      step(j + 1, S1, S, P1, P);
+      step(kGeneralStep, j, S, S1, P, P1);
+      step(kGeneralStep, j + 1, S1, S, P1, P);
     }
     check(n - 1, P, lsp, op);
     // P.V of the last tile.
