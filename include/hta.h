@@ -97,9 +97,9 @@ enum hta_device_status {
 
 /* Prefix-kernel implementation (see hta_plan_t.path). MFMA: bf16 with
  * G*T >= 16 query rows per KV head (32-row matrix-core blocks). DOT: bf16,
- * D = 128, G*T <= 16 (dot products on the vector ALUs, cross-lane reductions,
- * up to 8 rows per workgroup; the drafter's cross-attention shape). VALU:
- * float32, and everything else. */
+ * D = 128 or 64, G*T <= 16 (dot products on the vector ALUs, cross-lane
+ * reductions, up to 8 rows per workgroup; the drafter's cross-attention
+ * shape). VALU: float32, and everything else. */
 enum hta_path { HTA_PATH_AUTO = 0, HTA_PATH_MFMA = 1, HTA_PATH_VALU = 2, HTA_PATH_DOT = 3 };
 
 typedef struct {
@@ -113,7 +113,7 @@ typedef struct {
   float softmax_scale;    /* <= 0 selects 1/sqrt(D) */
   int32_t num_workgroups; /* prefix-kernel workgroups; 0 = sized from the device */
   int32_t force_path;     /* enum hta_path; AUTO picks MFMA for bf16 with G*T >= 16, DOT for
-                             bf16 with D = 128 and G*T <= 15, else VALU */
+                             bf16 with G*T <= 15, else VALU */
   int32_t qblocks_per_wave; /* MFMA path: 32-row query blocks per wave, 1 or 2; 0 = planned */
   int32_t fuse_merge;       /* MFMA path, hta_verify_attn: 1 = merge inside the split-KV launch
                                (see hta_verify_attn), 0 = separate merge launch (default) */
@@ -170,7 +170,7 @@ HTA_API int hta_verify_attn(hta_handle_t h, const void* q, const void* k_cache, 
  * [B,Hkv,Lcap,D]; out [B,Hq,T,D] in the handle's dtype, lse [B,Hq,T] float32
  * natural log. A sequence with prefix_len 0 gets out = 0 and lse = -inf; a
  * prefix_len outside [0, Lcap] gives NaN rows + HTA_STATUS_BAD_PREFIX.
- * bf16 handles with D = 128 and G*T <= 15 run the DOT kernel. Same split-KV kernel and
+ * bf16 handles with G*T <= 15 run the DOT kernel. Same split-KV kernel and
  * merge as hta_verify_attn, without the tree tile. Pointers as there. */
 HTA_API int hta_cross_attn(hta_handle_t h, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* prefix_len, void* out, float* lse, void* stream);

@@ -142,7 +142,7 @@ int plan_launch(const hta_config_t* cfg, int cus, Dims* dp, PrefixLaunch* pl, in
   plan_rows(d, path, cfg->qblocks_per_wave, pl);
   if (path == HTA_PATH_MFMA && !prefix_mfma_supported(d.D, pl->waves, pl->qb)) return HTA_ERR_UNSUPPORTED;
   const int occ = path == HTA_PATH_MFMA  ? prefix_mfma_occupancy(d.D, pl->waves, pl->qb)
-                  : path == HTA_PATH_DOT ? prefix_dot_occupancy(d.M)
+                  : path == HTA_PATH_DOT ? prefix_dot_occupancy(d.D, d.M)
                                          : prefix_valu_occupancy(d.D, d.bf16);
   int64_t nwg = cfg->num_workgroups;
   if (nwg <= 0) {

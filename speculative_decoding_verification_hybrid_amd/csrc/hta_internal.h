@@ -83,7 +83,7 @@ int plan_launch(const hta_config_t* cfg, int cus, Dims* d, PrefixLaunch* pl, int
 // The planned split-KV launch (any path) into `slots`; HTA_OK or HTA_ERR_HIP.
 int launch_split(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots, int* err_b,
                  int* status, hipStream_t s);
-// Small-M bf16 split-KV kernel (v_dot2 + DPP; D = 128, at most kDotMaxRows
+// Small-M bf16 split-KV kernel (v_dot2 + DPP; D = 128 or 64, at most kDotMaxRows
 // query rows per KV head, in dot_row_groups(M) groups of up to 8 on grid.y).
 // Float slots, same split and tree fusion.
 constexpr int kDotMaxRows = 16;
@@ -91,7 +91,7 @@ hipError_t launch_prefix_dot(const Dims& d, const PrefixLaunch& pl, const Prefix
                              int* err_b, int* status, hipStream_t s);
 bool prefix_dot_supported(int D, int M, bool bf16);
 int dot_row_groups(int M);
-int prefix_dot_occupancy(int M);
+int prefix_dot_occupancy(int D, int M);
 // The drafter's sliding-window self-attention over a ring of W = Lcap slots
 // with T new tokens (window.hip), and the append of the new tokens to the
 // ring (count: the B arrival counters shared with the commit).

@@ -1,5 +1,5 @@
 // Split-KV attention for bf16 layers with few query rows per KV head
-// (M = G*T <= 16): the drafter's cross-attention over the target's KV cache
+// (M = G*T <= 16, D = 128 or 64): the drafter's cross-attention over the target's KV cache
 // (LongSpec summary pages, §2.A "memory-efficient architecture": the draft
 // model reads the target model's cache instead of keeping its own), and
 // verification of very small trees. With so few rows a 32-row MFMA block would
@@ -10,24 +10,26 @@
 // to 8 (grid.y); the two workgroups of one range run side by side on one XCD,
 // so the second reads the keys and values from its L2.
 //
-// Layout of one wave (64 lanes = 4 groups of 16): lane (grp, c) loads the 16
-// bytes at dims 8c..8c+7 of one token per load, so a single 16-byte load of
-// the wave covers 4 consecutive tokens, fully coalesced. A unit is 8 such
-// loads (32 tokens) of K and of V straight into registers; the four waves of
-// a workgroup take the units of their range in turn. The next unit's K is
+// Layout of one wave at D = 128 (64 lanes = 4 groups of 16; at D = 64, 8
+// groups of 8): lane (grp, c) loads the 16 bytes at dims 8c..8c+7 of one
+// token per load, so a single 16-byte load of the wave covers 4 (8)
+// consecutive tokens, fully coalesced. A unit is 8 (4) such loads, 32
+// tokens, of K and of V straight into registers; the four waves of a
+// workgroup take the units of their range in turn. The next unit's K is
 // requested right after the scores are formed and its V right after P*V, so
 // one buffer each suffices and several waves fit per SIMD. No LDS staging.
 //
-// Per unit: every lane forms 8*MR partial dot products (8 dims each) for its
+// Per unit: every lane forms U*MR partial dot products (8 dims each) for its
 // tokens and the MR query rows, then four halving exchange stages (partners
-// at lane distance 8, mirrored within 8, 2, 1) sum them over the 16 lanes of
-// a group while halving the set each lane keeps: afterwards lane (grp, c)
-// holds the full scores of token slot c/2 for rows (c&1)*MR/2 .. +MR/2-1.
+// at lane distance 8, mirrored within 8, 2, 1; the first is skipped at
+// D = 64) sum them over the lanes of a token while halving the set each lane
+// keeps: afterwards lane (grp, c) holds the full scores of token slot c/2
+// for rows (c&1)*MR/2 .. +MR/2-1.
 // Online softmax in the log2 domain with a lazy maximum (raised only when a
 // row's unit maximum exceeds it by more than 8, so p <= 2^8). The
 // probabilities go through a 256-byte LDS buffer per wave as bf16 pairs of
 // neighbouring token slots, which v_dot2 multiplies into the output with the
-// matching V pair (two tokens' values of one dim packed by v_perm). The four
+// matching V pair (two tokens' values of one dim packed by v_perm). The token
 // groups' outputs and the four waves' states are combined once per piece.
 #include "common.h"
 #include "hta_internal.h"
@@ -36,9 +38,7 @@ namespace hta {
 namespace {
 
 constexpr int NK = kTileTokens;  // 64-token tiles of the split
-constexpr int D = 128;
-constexpr int U = 8;             // loads per unit of K (and of V): 4 tokens each
-constexpr int UNIT = 4 * U;      // tokens per unit
+constexpr int UNIT = 32;         // tokens per unit of K (and of V)
 constexpr int NWAVE = 4;
 constexpr float kLazy = 8.f;     // log2 units a row maximum may lag behind
 
@@ -79,7 +79,7 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b) {
   return dot2(a[3], b[3], acc);
 }
 
-// Sum (or max) over the 4 lane groups of 16.
+// Sum (or max) over the 4 lane groups of 16 (bits 4 and 5 of the lane).
 __device__ __forceinline__ float groups_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -105,11 +105,18 @@ __device__ __forceinline__ void halve(float* x, bool h) {
   }
 }
 
-template <int MR>
+// Lanes of one token's row: CL = D/8 lanes of 8 dims each, so one 16-byte load
+// of the wave covers TPL = 64/CL consecutive tokens and a unit is U = UNIT/TPL
+// loads. Lane (grp, c) = (lane / CL, lane % CL).
+template <int D, int MR>
 __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
-  constexpr int NV = MR / 2;  // scores per lane per unit
+  constexpr int CL = D / 8;     // lanes per token
+  constexpr int TPL = 64 / CL;  // tokens per load
+  constexpr int U = UNIT / TPL;  // loads per unit
+  constexpr int NV = MR / 2;    // scores per lane per unit
   static_assert(MR == 2 || MR == 4 || MR == 8, "rows per KV head");
-  __shared__ __align__(16) unsigned short pbuf[NWAVE][4][U / 2][MR][2];  // bf16 P: [wave][grp][slot pair][row][slot&1]
+  static_assert(D == 128 || D == 64, "head dims");
+  __shared__ __align__(16) unsigned short pbuf[NWAVE][TPL][U / 2][MR][2];  // bf16 P: [wave][grp][slot pair][row][slot&1]
   __shared__ __align__(16) float red_o[NWAVE][MR][D];
   __shared__ float red_m[NWAVE][MR];
   __shared__ float red_l[NWAVE][MR];
@@ -125,7 +132,7 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile bases stay scalar
-  const int grp = lane >> 4, c = lane & 15;
+  const int grp = lane / CL, c = lane % CL;
   const int slot_own = c >> 1;     // token slot of this lane's scores
   const int rbase = (c & 1) * NV;  // first row of this lane's scores
   const int r0 = (int)blockIdx.y * MR;  // this workgroup's first row
@@ -206,11 +213,11 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       if (t0 + UNIT <= nvalid) {  // the whole unit is valid: one address, constant offsets
         const unsigned off = (unsigned)((t0 + grp) * D + 8 * c) * 2u;
 #pragma unroll
-        for (int u = 0; u < U; ++u) dst[u] = *(const u32x4*)(sb + off + u * 4 * D * 2);
+        for (int u = 0; u < U; ++u) dst[u] = *(const u32x4*)(sb + off + u * TPL * D * 2);
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const unsigned tk = (unsigned)min(t0 + 4 * u + grp, nvalid - 1);
+          const unsigned tk = (unsigned)min(t0 + TPL * u + grp, nvalid - 1);
           dst[u] = *(const u32x4*)(sb + (tk * D + 8u * c) * 2u);
         }
       }
@@ -238,12 +245,14 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       // (that would need a second buffer and halve the waves per SIMD)
       __builtin_amdgcn_sched_barrier(0);
       if (i + 1 < nun) load_rows(unit_of(i + 1), ktg, kg, kr);
-      halve<kRor8, U * MR / 2>(xs, (c >> 3) & 1);
-      halve<kHalfMirror, U * MR / 4>(xs, (c >> 2) & 1);
-      halve<kXor2, U * MR / 8>(xs, (c >> 1) & 1);
-      halve<kXor1, U * MR / 16>(xs, c & 1);
+      // (at D = 64 the 8 lanes of a token start at the second stage, with
+      // the same 4 * MR values left as after the first stage at D = 128)
+      if constexpr (CL == 16) halve<kRor8, 4 * MR>(xs, (c >> 3) & 1);
+      halve<kHalfMirror, 2 * MR>(xs, (c >> 2) & 1);
+      halve<kXor2, MR>(xs, (c >> 1) & 1);
+      halve<kXor1, MR / 2>(xs, c & 1);
       // xs[j], j < NV: score of token slot slot_own, row rbase + j
-      const int tk = (pu & 1) * UNIT + 4 * slot_own + grp;
+      const int tk = (pu & 1) * UNIT + TPL * slot_own + grp;
       float s[NV], um[NV];
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
@@ -337,7 +346,10 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
 #pragma unroll
     for (int r = 0; r < MR; ++r)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[r][e] = groups_sum(o[r][e]);
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (CL == 8) o[r][e] += dpp<kRor8>(o[r][e]);  // lane bit 3 is a token group here
+        o[r][e] = groups_sum(o[r][e]);
+      }
     if (grp == 0) {
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
@@ -384,21 +396,25 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
 typedef void (*KernelFn)(DotArgs);
 
 // Rows per workgroup for M rows in all (two groups of up to 8 above 8 rows).
-KernelFn pick(int M) {
-  if (M <= 2) return prefix_dot_kernel<2>;
-  if (M <= 4) return prefix_dot_kernel<4>;
-  if (M <= kDotMaxRows) return prefix_dot_kernel<8>;
+template <int D>
+KernelFn pick_d(int M) {
+  if (M <= 2) return prefix_dot_kernel<D, 2>;
+  if (M <= 4) return prefix_dot_kernel<D, 4>;
+  if (M <= kDotMaxRows) return prefix_dot_kernel<D, 8>;
   return nullptr;
 }
+KernelFn pick(int D, int M) { return D == 128 ? pick_d<128>(M) : D == 64 ? pick_d<64>(M) : nullptr; }
 
 }  // namespace
 
-bool prefix_dot_supported(int D_, int M, bool bf16) { return bf16 && D_ == D && M >= 1 && M <= kDotMaxRows; }
+bool prefix_dot_supported(int D, int M, bool bf16) {
+  return bf16 && (D == 128 || D == 64) && M >= 1 && M <= kDotMaxRows;
+}
 
 int dot_row_groups(int M) { return M > 8 ? 2 : 1; }
 
-int prefix_dot_occupancy(int M) {
-  KernelFn k = pick(M);
+int prefix_dot_occupancy(int D, int M) {
+  KernelFn k = pick(D, M);
   if (!k) return 0;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), 256, 0) !=
@@ -409,8 +425,8 @@ int prefix_dot_occupancy(int M) {
 
 hipError_t launch_prefix_dot(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, Slots slots,
                              int* err_b, int* status, hipStream_t s) {
-  KernelFn k = pick(d.M);
-  if (!k || d.D != D || !d.bf16 || pl.row_groups != dot_row_groups(d.M)) return hipErrorInvalidValue;
+  KernelFn k = pick(d.D, d.M);
+  if (!k || !d.bf16 || pl.row_groups != dot_row_groups(d.M)) return hipErrorInvalidValue;
   DotArgs a;
   a.q = in.q;
   a.k = in.k_cache;

@@ -69,7 +69,7 @@ def test_named_workloads_validate(lib, key):
     (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=4), hta.HTA_OK),                  # 4 x 4 rows
     (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=5), hta.HTA_ERR_UNSUPPORTED),     # 4 x 5 rows > 16
     (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2, dtype="f32"), hta.HTA_ERR_UNSUPPORTED),
-    (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2, head_dim=64), hta.HTA_ERR_UNSUPPORTED),
+    (dict(force_path=hta.HTA_PATH_DOT, tree_nodes=2, head_dim=64), hta.HTA_OK),                # D = 64, 8 rows
     (dict(force_path=hta.HTA_PATH_MFMA, dtype="f32"), hta.HTA_ERR_UNSUPPORTED),
     (dict(softmax_scale=math.nan), hta.HTA_ERR_INVALID_ARG),
     (dict(kv_capacity=1 << 30), hta.HTA_ERR_UNSUPPORTED),

@@ -43,6 +43,11 @@ CROSS = {
     "gqa4_t3_m12": dict(B=2, Hq=16, Hkv=4, D=128, Lcap=1200, T=3, prefix_len=[1200, 97]),     # M = 12: 2 groups
     "gqa5_t3_m15": dict(B=1, Hq=40, Hkv=8, D=128, Lcap=700, T=3, prefix_len=[700]),          # M = 15
     "mha_t9_ragged": dict(B=3, Hq=2, Hkv=2, D=128, Lcap=300, T=9, prefix_len=[300, 1, 65]),  # M = 9
+    "d64_m4_gqa4": dict(B=2, Hq=16, Hkv=4, D=64, Lcap=1500, T=1, prefix_len=[1500, 333]),      # D = 64
+    "d64_m1_mha_ragged": dict(B=4, Hq=4, Hkv=4, D=64, Lcap=300, T=1, prefix_len=[1, 63, 64, 300]),
+    "d64_m8_t2": dict(B=1, Hq=8, Hkv=2, D=64, Lcap=900, T=2, prefix_len=[899]),
+    "d64_m12_t3": dict(B=2, Hq=16, Hkv=4, D=64, Lcap=700, T=3, prefix_len=[700, 65]),          # two row groups
+    "d64_poison_tail": dict(B=2, Hq=8, Hkv=2, D=64, Lcap=400, T=1, prefix_len=[97, 1], poison_tail=True),
     "poison_tail": dict(B=3, Hq=8, Hkv=2, D=128, Lcap=500, T=1, prefix_len=[77, 500, 1], poison_tail=True),
     "unit_tails": dict(B=5, Hq=8, Hkv=2, D=128, Lcap=200, T=1, prefix_len=[31, 32, 33, 95, 97]),
     "drift_keys": dict(B=1, Hq=32, Hkv=8, D=128, Lcap=5000, T=1, prefix_len=[5000], drift=True),
@@ -108,6 +113,10 @@ SMALL_TREES = {
     "t5_chain_mha": dict(B=1, Hq=2, Hkv=2, D=128, Lcap=300, T=5, prefix_len=[257], parents=[tree_chain(5)]),
     "t4_gqa2_forest": dict(B=1, Hq=4, Hkv=2, D=128, Lcap=128, T=4, prefix_len=[128], parents=[[-1, 0, -1, 2]]),
     "t9_mha": dict(B=2, Hq=2, Hkv=2, D=128, Lcap=700, T=9, prefix_len=[700, 65]),
+    "d64_t6_mha_forest": dict(B=2, Hq=2, Hkv=2, D=64, Lcap=500, T=6, prefix_len=[500, 70],
+                              parents=[[-1, 0, 1, -1, 3, 0], [-1, 0, 0, 1, 2, 4]]),
+    "d64_t3_gqa4_m12": dict(B=1, Hq=8, Hkv=2, D=64, Lcap=1000, T=3, prefix_len=[999]),
+    "d64_t1_gqa4": dict(B=3, Hq=8, Hkv=2, D=64, Lcap=256, T=1, prefix_len=[256, 0, 17]),
     "t3_gqa4_m12": dict(B=2, Hq=8, Hkv=2, D=128, Lcap=1000, T=3, prefix_len=[1000, 64]),
     "t5_gqa3_m15_chain": dict(B=1, Hq=6, Hkv=2, D=128, Lcap=400, T=5, prefix_len=[399], parents=[tree_chain(5)]),
     "t7_gqa2_m14_forest": dict(B=1, Hq=4, Hkv=2, D=128, Lcap=256, T=7, prefix_len=[130],
