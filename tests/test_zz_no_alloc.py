@@ -84,3 +84,36 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     with pytest.raises(hta.HtaError) as e:
         _noalloc(w, dev, **big_cfg)
     assert e.value.code == hta.HTA_ERR_TOO_LARGE
+
+
+def test_noalloc_under_graph_capture():
+    """Captured once, replayed with other no-allocation calls (sharing the scratch array) in between."""
+    w = make_custom(seed=11, B=2, Hq=16, Hkv=4, D=128, Lcap=1500, T=16, prefix_len=[1500, 612], dtype="bf16")
+    w2 = make_custom(seed=12, B=1, Hq=4, Hkv=1, D=128, Lcap=900, T=2, prefix_len=[900], dtype="bf16")  # DOT path
+    dev, dev2 = to_device(w), to_device(w2)
+    say("hta_verify_attn_noalloc graph: eager")
+    ref_o, ref_l, st = _noalloc(w, dev)
+    assert st == 0
+    ref2_o, ref2_l, st2 = _noalloc(w2, dev2)
+    assert st2 == 0
+    cfg = config_for(w)
+    out = torch.empty(w.B, w.Hq, w.T, w.D, dtype=io_dtype(w), device="cuda")
+    lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["k_tree"], dev["v_tree"], dev["parent"], dev["prefix_len"])
+    say("hta_verify_attn_noalloc graph: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hta.hta_verify_attn_noalloc(cfg, *args, out, lse, status, torch.cuda.current_stream())
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        say(f"hta_verify_attn_noalloc graph: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref_o)
+        assert np.array_equal(lse.cpu().numpy().astype(np.float64), ref_l)
+        o2, l2, s2 = _noalloc(w2, dev2)  # another shape through the same scratch array
+        assert s2 == 0 and np.array_equal(o2, ref2_o) and np.array_equal(l2, ref2_l)
+    assert int(status.item()) == 0
