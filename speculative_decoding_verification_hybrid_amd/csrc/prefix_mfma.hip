@@ -34,7 +34,9 @@
 // fragments during tile j, and its V registers are consumed during tile j+1,
 // so at the start of tile j the stage of tile j-2 is free everywhere: after
 // one workgroup barrier (which also publishes every wave's copies of tile
-// j+1) it is refilled with tile j-2+NS, leaving NS-3 tiles in flight. Each
+// j+1) it is refilled with tile j-2+NS (with the NS = 4 stages used, tile
+// j+2: one tile in flight while tile j runs, which keeps up, since the loop
+// is bound by its own instruction stream rather than by the memory). Each
 // wave waits for its own copies with an explicit vmcnt; the copies (and the Q
 // loads, queued ahead of them) come from inline assembly so the compiler's
 // wait insertion never drains the copy queue before an LDS read.
@@ -339,12 +341,9 @@ __global__ void __launch_bounds__(NWAVE * 64) prefix_mfma_kernel(PrefixArgs a) {
       }
     }
 
-    // Prologue: queue tile 0, the Q loads and tile 1 only, wait for tile 0
-    // and Q, score tile 0. Every CU asking for all its stages at once (every
-    // workgroup does this at the same moment) would keep its waves blocked on
-    // issuing copies until most of those bytes had arrived; the other stages
-    // are filled during the first tiles instead (two tiles per tile until the
-    // ring is full).
+    // Prologue: queue tile 0, the Q loads and tile 1 (P0 = NS - 2 tiles: the
+    // steady refill of tile 0 then queues tile 2), wait for tile 0 and Q,
+    // score tile 0.
     constexpr int P0 = 2;
     copy_tile(0);
     // Q^T fragments (B operand of S^T = K.Q^T): row rowq[X], dims 16c + 8hh .. +7.
