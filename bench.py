@@ -26,7 +26,8 @@ the oracle's accept + commit on the same inputs beside it. A third leg
 ("draft_cross_attn") times the drafter's cross-attention over the same 32k
 cache with one draft token (hta_cross_attn, the small-row DOT kernel), and a
 fourth ("tree_build") the construction of the next draft tree from the last
-logits and a 32k-token history (hta_build_tree). "configs" reports the layer
+logits and a 32k-token history (hta_build_tree; its "indexed" object times
+hta_build_tree_indexed in a decoding loop that adds 3 tokens per call). "configs" reports the layer
 at all five configurations (p10/p50/p90 over graph replays, each against the
 HBM peak and against a measured device copy, with one oracle run each), and
 "copy_bw_gbs" that copy's bandwidth.
@@ -362,6 +363,61 @@ def draft_cross_row(w, steps, warmup, replica_bytes, cpu_seconds):
 TREE_KEEP = [8, 6, 5, 4, 4, 3, 3, 2, 2, 2, 1, 1, 1, 1, 1]  # tokens kept per guess rank (non-increasing)
 
 
+def tree_indexed_leg(h, case, lg, hist, params, m, steps, warmup):
+    """hta_build_tree_indexed in a decoding loop: each call finds 3 more history
+    tokens than the last (the accepted ones), adds their grams to the index and
+    answers the queries from it. Before every timed graph replay the index is
+    reset and brought to the length just below the first call's (untimed), so
+    every replayed call inserts exactly 3 positions."""
+    import torch
+    from speculative_decoding_verification_hybrid_amd import hta
+
+    B, cap = case.history.shape
+    T = int(h.dims[4])
+    add = 3
+    L0 = cap - add * steps
+    lens = [torch.tensor([L0 + add * i], dtype=torch.int32, device="cuda") for i in range(steps)]
+    pre = torch.tensor([L0 - add], dtype=torch.int32, device="cuda")
+    tok = torch.empty(1, T, dtype=torch.int32, device="cuda")
+    par = torch.empty(1, T, dtype=torch.int32, device="cuda")
+    nn = torch.empty(1, dtype=torch.int32, device="cuda")
+    idx = hta.hta_ngram_index_create(B, cap, m)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def prime():
+        hta.hta_ngram_index_reset(idx, -1, s)
+        e0.record(s)
+        hta.hta_build_tree_indexed(h, idx, lg, hist, pre, params, tok, par, nn, s)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    for _ in range(max(1, warmup)):
+        build_us = prime()
+        for i in range(steps):
+            hta.hta_build_tree_indexed(h, idx, lg, hist, lens[i], params, tok, par, nn, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream()
+        for i in range(steps):
+            hta.hta_build_tree_indexed(h, idx, lg, hist, lens[i], params, tok, par, nn, cs)
+    build_us = prime()
+    g.replay()
+    prime()
+    e0.record(s)
+    g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    hta.hta_ngram_index_destroy(idx)
+    return {"us_per_call": round(ms * 1e3, 3), "new_tokens_per_call": add,
+            "history_len": f"{L0}..{L0 + add * (steps - 1)}", "n_nodes_last": int(nn.item()),
+            "index_first_build_us": round(build_us, 1),
+            "index_first_build": f"{L0 - add} positions into an empty index (one call)"}
+
+
 def tree_build_row(w, steps, warmup, cpu_seconds):
     """hta_build_tree for one sequence: the last logits over the Llama-3.1-8B vocabulary
     (bf16), a 32k-token history, 15 next-next guesses, 3-grams, a 64-node tree. The
@@ -401,16 +457,20 @@ def tree_build_row(w, steps, warmup, cpu_seconds):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     status = hta.hta_get_status(h)
+    n_scan = int(nn.item())
+    indexed = tree_indexed_leg(h, case, lg, hist, params, m, steps, warmup)
+    status_ix = hta.hta_get_status(h)
     hta.hta_destroy(h)
     nbytes = VOCAB * 2 + cap * 4 + w.T * 8 + 4
     row = {
         "workload": f"tree construction: bf16 logits V={VOCAB}, {cap}-token history, k={k} guesses, {m}-grams, "
                     f"{w.T}-node tree",
         "us_per_call": round(ms * 1e3, 3),
-        "n_nodes": int(nn.item()),
-        "status_ok": status == 0,
+        "n_nodes": n_scan,
+        "status_ok": status == 0 and status_ix == 0,
         "bytes_per_call": nbytes,
         "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "indexed": indexed,
     }
     if cpu_seconds > 0:
         import oracle

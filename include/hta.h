@@ -234,6 +234,48 @@ HTA_API int hta_build_tree(hta_handle_t h, const void* logits, int32_t vocab, in
                            const hta_tree_params_t* params, int32_t* tree_tokens, int32_t* parent,
                            int32_t* n_nodes, void* stream);
 
+/* A hash index of the m-grams of B token histories, so that the retrieval of
+ * hta_build_tree_indexed costs a few table probes per query instead of a pass
+ * over the whole history (LogitSpec summary pages, §4 "experimental results",
+ * overhead: the retrieval is hash-based and adds about 1 % of the wall time).
+ * Per sequence it maps each distinct m-gram of history[b][0 .. n) to the
+ * largest end position at which it occurs, where n = the history length it
+ * has been brought up to (kept on the device). Open addressing with linear
+ * probing over 2^s slots, 2^s >= 2 * history_cap; a slot holds the end
+ * position of the gram's first inserted occurrence (its key, compared token
+ * by token against the history, so results never depend on hash collisions)
+ * and the largest end position seen. Device memory: B * 2^s * 8 bytes + 8 B
+ * bytes, allocated on the current HIP device. */
+typedef struct hta_ngram_index_s* hta_ngram_index_t;
+
+/* Creates an empty index for batch sequences of history_cap tokens and grams
+ * of m tokens (1 .. HTA_MAX_NGRAM). On failure *out is NULL; returns
+ * HTA_ERR_INVALID_ARG for parameters out of range, HTA_ERR_UNSUPPORTED for
+ * history_cap > 2^26, HTA_ERR_NO_MEMORY if the table cannot be allocated. */
+HTA_API int hta_ngram_index_create(hta_ngram_index_t* out, int32_t batch, int32_t history_cap, int32_t m);
+
+/* Frees the index (synchronises the device first). NULL is accepted. */
+HTA_API int hta_ngram_index_destroy(hta_ngram_index_t idx);
+
+/* Empties sequence seq's part of the index (seq = -1: every sequence), on the
+ * stream, with a fill kernel (no memset node: capturable). Required before a
+ * batch slot starts a new sequence whose first tokens differ from the old
+ * one's. seq outside [-1, batch) gives HTA_ERR_INVALID_ARG. */
+HTA_API int hta_ngram_index_reset(hta_ngram_index_t idx, int32_t seq, void* stream);
+
+/* hta_build_tree with the retrieval through idx: the same outputs, the same
+ * status rules and the same argument rules (history_cap is the index's; the
+ * handle's batch and params->m must equal the index's, else
+ * HTA_ERR_INVALID_ARG). First the grams ending at positions [n, history_len[b])
+ * are added to sequence b's part of the index; a history_len[b] below n
+ * (the sequence was cut back) rebuilds that part from position 0. The tokens
+ * history[b][0 .. n) must not have changed since they were added (reset the
+ * sequence otherwise). Calls with one index must not overlap. */
+HTA_API int hta_build_tree_indexed(hta_handle_t h, hta_ngram_index_t idx, const void* logits, int32_t vocab,
+                                   int32_t logits_dtype, const int32_t* history, const int32_t* history_len,
+                                   const hta_tree_params_t* params, int32_t* tree_tokens, int32_t* parent,
+                                   int32_t* n_nodes, void* stream);
+
 /* The tree mask alone: mask_out[b][i] (uint64, device) has bit j set iff
  * tree node j is node i or one of its ancestors. A sequence whose parent
  * array breaks the rule gets all-zero words and sets HTA_STATUS_BAD_TREE.

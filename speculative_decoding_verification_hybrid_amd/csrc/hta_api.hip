@@ -27,6 +27,11 @@ struct hta_handle_s {
   bool fuse_merge;                  // hta_verify_attn merges inside the split-KV launch
 };
 
+struct hta_ngram_index_s {
+  hta::NgramIndex ix;  // table [B][2^slots_log2][2], len [B], in one allocation
+  int device;
+};
+
 namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -172,6 +177,25 @@ int launch_split(const Dims& d, const PrefixLaunch& pl, const PrefixInputs& in, 
 }
 
 }  // namespace hta
+
+namespace {
+// The tree-building arguments shared by hta_build_tree and its indexed form.
+int tree_params(const hta_tree_params_t* params, int32_t vocab, int32_t logits_dtype, hta::TreeParams* p) {
+  if (logits_dtype != HTA_F32 && logits_dtype != HTA_BF16) return HTA_ERR_INVALID_ARG;
+  if (params->k < 0 || params->k > HTA_MAX_TREE_GUESSES || params->m < 1 || params->m > HTA_MAX_NGRAM ||
+      params->keep_first < 0 || params->keep_first > 64)
+    return HTA_ERR_INVALID_ARG;
+  for (int r = 0; r < params->k; ++r)
+    if (params->keep[r] < 0 || params->keep[r] > 64) return HTA_ERR_INVALID_ARG;
+  if (vocab < params->k + 1) return HTA_ERR_INVALID_ARG;
+  if (hta::topk_split_for(vocab) > hta::kMaxTreeSplit) return HTA_ERR_UNSUPPORTED;
+  p->k = params->k;
+  p->m = params->m;
+  p->keep_first = params->keep_first;
+  for (int r = 0; r < hta::kMaxTreeGuesses; ++r) p->keep[r] = r < params->k ? params->keep[r] : 0;
+  return HTA_OK;
+}
+}  // namespace
 
 static int launch_split(hta_handle_t h, const hta::PrefixInputs& in, hipStream_t s) {
   return hta::launch_split(h->dims, h->pl, in, h->slots, h->err_b, h->status, s);
@@ -366,22 +390,80 @@ int hta_build_tree(hta_handle_t h, const void* logits, int32_t vocab, int32_t lo
                    int32_t* tree_tokens, int32_t* parent, int32_t* n_nodes, void* stream) {
   if (!h || !logits || !history || !history_len || !params || !tree_tokens || !parent || !n_nodes)
     return HTA_ERR_INVALID_ARG;
-  if (logits_dtype != HTA_F32 && logits_dtype != HTA_BF16) return HTA_ERR_INVALID_ARG;
-  if (params->k < 0 || params->k > HTA_MAX_TREE_GUESSES || params->m < 1 || params->m > HTA_MAX_NGRAM ||
-      params->keep_first < 0 || params->keep_first > 64 || history_cap < 1)
-    return HTA_ERR_INVALID_ARG;
-  for (int r = 0; r < params->k; ++r)
-    if (params->keep[r] < 0 || params->keep[r] > 64) return HTA_ERR_INVALID_ARG;
-  if (vocab < params->k + 1) return HTA_ERR_INVALID_ARG;
-  if (hta::topk_split_for(vocab) > hta::kMaxTreeSplit) return HTA_ERR_UNSUPPORTED;
+  if (history_cap < 1) return HTA_ERR_INVALID_ARG;
   hta::TreeParams p;
-  p.k = params->k;
-  p.m = params->m;
-  p.keep_first = params->keep_first;
-  for (int r = 0; r < hta::kMaxTreeGuesses; ++r) p.keep[r] = r < params->k ? params->keep[r] : 0;
+  const int rc = tree_params(params, vocab, logits_dtype, &p);
+  if (rc != HTA_OK) return rc;
   return check_hip(hta::launch_build_tree(h->dims, logits, vocab, logits_dtype == HTA_BF16, history, history_cap,
                                           history_len, p, h->topk_part, h->tree_aux, tree_tokens, parent, n_nodes, h->status,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int hta_ngram_index_create(hta_ngram_index_t* out, int32_t batch, int32_t history_cap, int32_t m) {
+  if (!out) return HTA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (batch < 1 || history_cap < 1 || m < 1 || m > HTA_MAX_NGRAM) return HTA_ERR_INVALID_ARG;
+  if (history_cap > (1 << 26) || batch > (1 << 20)) return HTA_ERR_UNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HTA_ERR_NO_DEVICE;
+  int lg = 6;  // at least 64 slots, and at least twice the positions of a history
+  while (((int64_t)1 << lg) < 2 * (int64_t)history_cap) ++lg;
+  const size_t tab_bytes = (size_t)batch * ((size_t)hta::ngram_slot_ints(m) << lg) * sizeof(int);
+  const size_t bytes = align256(tab_bytes) + (size_t)batch * sizeof(int);
+  hta_ngram_index_s* x = new (std::nothrow) hta_ngram_index_s();
+  if (!x) return HTA_ERR_NO_MEMORY;
+  void* mem = nullptr;
+  if (hipMalloc(&mem, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete x;
+    return HTA_ERR_NO_MEMORY;
+  }
+  x->ix.table = static_cast<int*>(mem);
+  x->ix.len = reinterpret_cast<int*>(static_cast<char*>(mem) + align256(tab_bytes));
+  x->ix.B = batch;
+  x->ix.cap = history_cap;
+  x->ix.m = m;
+  x->ix.slots_log2 = lg;
+  x->device = dev;
+  if (hta::launch_ngram_reset(x->ix, -1, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(mem);
+    delete x;
+    return HTA_ERR_HIP;
+  }
+  *out = x;
+  return HTA_OK;
+}
+
+int hta_ngram_index_destroy(hta_ngram_index_t idx) {
+  if (!idx) return HTA_OK;
+  int rc = HTA_OK;
+  int cur = 0;
+  if (hipGetDevice(&cur) == hipSuccess && cur != idx->device) (void)hipSetDevice(idx->device);
+  if (hipDeviceSynchronize() != hipSuccess) rc = HTA_ERR_HIP;
+  if (hipFree(idx->ix.table) != hipSuccess) rc = HTA_ERR_HIP;
+  if (cur != idx->device) (void)hipSetDevice(cur);
+  delete idx;
+  return rc;
+}
+
+int hta_ngram_index_reset(hta_ngram_index_t idx, int32_t seq, void* stream) {
+  if (!idx || seq < -1 || seq >= idx->ix.B) return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_ngram_reset(idx->ix, seq, static_cast<hipStream_t>(stream)));
+}
+
+int hta_build_tree_indexed(hta_handle_t h, hta_ngram_index_t idx, const void* logits, int32_t vocab,
+                           int32_t logits_dtype, const int32_t* history, const int32_t* history_len,
+                           const hta_tree_params_t* params, int32_t* tree_tokens, int32_t* parent, int32_t* n_nodes,
+                           void* stream) {
+  if (!h || !idx || !logits || !history || !history_len || !params || !tree_tokens || !parent || !n_nodes)
+    return HTA_ERR_INVALID_ARG;
+  hta::TreeParams p;
+  const int rc = tree_params(params, vocab, logits_dtype, &p);
+  if (rc != HTA_OK) return rc;
+  if (idx->ix.B != h->dims.B || idx->ix.m != params->m) return HTA_ERR_INVALID_ARG;
+  return check_hip(hta::launch_build_tree_indexed(h->dims, logits, vocab, logits_dtype == HTA_BF16, history,
+                                                  history_len, p, h->topk_part, idx->ix, tree_tokens, parent,
+                                                  n_nodes, h->status, static_cast<hipStream_t>(stream)));
 }
 
 int hta_tree_mask(hta_handle_t h, const int32_t* parent, uint64_t* mask_out, void* stream) {

@@ -114,6 +114,24 @@ int topk_split_for(int V);
 hipError_t launch_build_tree(const Dims& d, const void* logits, int V, bool logits_bf16, const int* history,
                              int hist_cap, const int* hist_len, const TreeParams& p, unsigned long long* part,
                              int* aux, int* tokens, int* parent, int* n_nodes, int* status, hipStream_t s);
+// Hash index of the m-grams of B histories (tree_build.hip): per sequence
+// 2^slots_log2 slots of ngram_slot_ints(m) ints {end position of the key
+// occurrence (-1: empty), largest end position, the key's m tokens};
+// len[b] = the history length it covers.
+struct NgramIndex {
+  int* table;
+  int* len;
+  int B, cap, m, slots_log2;
+};
+// launch_build_tree with the retrieval through the index (brought up to
+// hist_len first).
+hipError_t launch_build_tree_indexed(const Dims& d, const void* logits, int V, bool logits_bf16, const int* history,
+                                     const int* hist_len, const TreeParams& p, unsigned long long* part,
+                                     const NgramIndex& ix, int* tokens, int* parent, int* n_nodes, int* status,
+                                     hipStream_t s);
+int ngram_slot_ints(int m);
+// Empties sequence seq's part of the index (seq < 0: all), with a fill kernel.
+hipError_t launch_ngram_reset(const NgramIndex& ix, int seq, hipStream_t s);
 // Occupancy (workgroups per CU) of the chosen prefix kernel, for sizing nwg.
 int prefix_mfma_occupancy(int D, int waves, int qb);
 int prefix_valu_occupancy(int D, bool bf16);

@@ -121,6 +121,11 @@ _SIGNATURES = {
     "hta_build_tree": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _vp, ctypes.POINTER(HtaTreeParams)]
                        + [_vp] * 3 + [_vp]),
     "hta_window_append": (ctypes.c_int, [_vp] * 6 + [_vp]),
+    "hta_ngram_index_create": (ctypes.c_int, [ctypes.POINTER(_vp), _i32, _i32, _i32]),
+    "hta_ngram_index_destroy": (ctypes.c_int, [_vp]),
+    "hta_ngram_index_reset": (ctypes.c_int, [_vp, _i32, _vp]),
+    "hta_build_tree_indexed": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(HtaTreeParams)]
+                               + [_vp] * 3 + [_vp]),
     "hta_prefix_partials": (ctypes.c_int, [_vp] * 5 + [_vp]),
     "hta_merge_prefix": (ctypes.c_int, [_vp] * 4 + [_vp]),
     "hta_lse_merge": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -360,6 +365,64 @@ def hta_build_tree(h: Handle, logits, history, history_len, params: HtaTreeParam
     _check(load_library().hta_build_tree(_vp(h.ptr), _vp(lp), V, ldt, _vp(hp), cap, _vp(args[0]),
                                          ctypes.byref(params), *[_vp(a) for a in outs], _vp(_stream_ptr(stream))),
            "hta_build_tree")
+
+
+class NgramIndex:
+    """An hta_ngram_index_t plus the sizes it was created with (for argument checks)."""
+
+    def __init__(self, ptr: int, batch: int, history_cap: int, m: int):
+        self.ptr = ptr
+        self.batch, self.history_cap, self.m = batch, history_cap, m
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        hta_ngram_index_destroy(self)
+
+
+def hta_ngram_index_create(batch: int, history_cap: int, m: int) -> NgramIndex:
+    out = _vp()
+    _check(load_library().hta_ngram_index_create(ctypes.byref(out), batch, history_cap, m), "hta_ngram_index_create")
+    return NgramIndex(out.value, batch, history_cap, m)
+
+
+def hta_ngram_index_destroy(idx: NgramIndex) -> None:
+    if idx.ptr:
+        code = load_library().hta_ngram_index_destroy(_vp(idx.ptr))
+        idx.ptr = None
+        _check(code, "hta_ngram_index_destroy")
+
+
+def hta_ngram_index_reset(idx: NgramIndex, seq: int = -1, stream=None) -> None:
+    """Empties sequence seq of the index (-1: every sequence), on the stream."""
+    _check(load_library().hta_ngram_index_reset(_vp(idx.ptr), int(seq), _vp(_stream_ptr(stream))),
+           "hta_ngram_index_reset")
+
+
+def hta_build_tree_indexed(h: Handle, idx: NgramIndex, logits, history, history_len, params: HtaTreeParams,
+                           tree_tokens, parent, n_nodes, stream=None) -> None:
+    """hta_build_tree with the retrieval through idx; history [B, idx.history_cap] int32."""
+    import torch
+    B, _, _, _, T, _ = h.dims
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits must be a [B, V] tensor")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"logits has dtype {logits.dtype}, expected float32 or bfloat16")
+    V = int(logits.shape[1])
+    ldt = HTA_BF16 if logits.dtype == torch.bfloat16 else HTA_F32
+    lp = _tensor(logits, "logits", logits.dtype, (B, V))
+    hp = _tensor(history, "history", torch.int32, (idx.batch, idx.history_cap))
+    lenp = _tensor(history_len, "history_len", torch.int32, (B,))
+    outs = [
+        _tensor(tree_tokens, "tree_tokens", torch.int32, (B, T)),
+        _tensor(parent, "parent", torch.int32, (B, T)),
+        _tensor(n_nodes, "n_nodes", torch.int32, (B,)),
+    ]
+    _check(load_library().hta_build_tree_indexed(_vp(h.ptr), _vp(idx.ptr), _vp(lp), V, ldt, _vp(hp), _vp(lenp),
+                                                 ctypes.byref(params), *[_vp(a) for a in outs],
+                                                 _vp(_stream_ptr(stream))),
+           "hta_build_tree_indexed")
 
 
 def hta_window_attn(h: Handle, q, k_ring, v_ring, k_new, v_new, pos, out, lse, stream=None) -> None:

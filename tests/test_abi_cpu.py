@@ -114,6 +114,25 @@ def test_null_arguments_fail_before_any_hip_call(lib):
     assert lib.hta_window_append(None, *([None] * 6)) == hta.HTA_ERR_INVALID_ARG
     assert lib.hta_build_tree(None, None, 100, hta.HTA_BF16, None, 10, None, None, None, None, None,
                               None) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_build_tree_indexed(None, None, None, 100, hta.HTA_BF16, None, None, None, None, None, None,
+                                      None) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_ngram_index_destroy(None) == hta.HTA_OK
+    assert lib.hta_ngram_index_reset(None, 0, None) == hta.HTA_ERR_INVALID_ARG
+    assert lib.hta_ngram_index_create(None, 1, 10, 3) == hta.HTA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("batch,cap,m,code", [
+    (0, 10, 3, hta.HTA_ERR_INVALID_ARG),
+    (1, 0, 3, hta.HTA_ERR_INVALID_ARG),
+    (1, 10, 0, hta.HTA_ERR_INVALID_ARG),
+    (1, 10, 9, hta.HTA_ERR_INVALID_ARG),
+    (1, (1 << 26) + 1, 3, hta.HTA_ERR_UNSUPPORTED),
+])
+def test_ngram_index_create_codes(lib, batch, cap, m, code):
+    # every one of these is rejected before the device is touched
+    out = ctypes.c_void_p(123)
+    assert lib.hta_ngram_index_create(ctypes.byref(out), batch, cap, m) == code
+    assert out.value is None
 
 
 def test_status_strings(lib):

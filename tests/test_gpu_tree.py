@@ -1,8 +1,14 @@
-"""GPU parity of hta_build_tree against the oracle (exact: token ids, parents, node counts).
+"""GPU parity of hta_build_tree and hta_build_tree_indexed against the oracle
+(exact: token ids, parents, node counts).
 
 Both sides rank on the same exact logit values (lower index first on ties)
-and search the same token sequence, so every output must be identical.
+and search the same token sequence, so every output must be identical. The
+indexed form answers the n-gram queries from a hash index of the history that
+it brings up to date on each call; every case below runs through both forms,
+and the index has tests of its own for growing, cut-back and reset histories.
 """
+
+import ctypes
 
 import numpy as np
 import pytest
@@ -16,32 +22,47 @@ from workloads import f32_to_bf16_bits, make_tree_case
 pytestmark = pytest.mark.gpu
 
 
-def _run(case, k, m, keep_first, keep, T, hist_len=None):
-    B = case.B
+def _logits(case):
     if case.dtype == "bf16":
-        lg = torch.from_numpy(np.ascontiguousarray(case.logits).view(np.int16)).view(torch.bfloat16).cuda()
-    else:
-        lg = torch.from_numpy(np.ascontiguousarray(case.logits, dtype=np.float32)).cuda()
+        return torch.from_numpy(np.ascontiguousarray(case.logits).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(case.logits, dtype=np.float32)).cuda()
+
+
+def _outs(B, T):
+    return (torch.full((B, T), -7, dtype=torch.int32, device="cuda"),
+            torch.full((B, T), -7, dtype=torch.int32, device="cuda"),
+            torch.full((B,), -7, dtype=torch.int32, device="cuda"))
+
+
+def _run(case, k, m, keep_first, keep, T, hist_len=None, indexed=False):
+    B = case.B
+    lg = _logits(case)
     hist = torch.from_numpy(case.history).cuda()
     hl = torch.from_numpy(np.asarray(case.history_len if hist_len is None else hist_len, dtype=np.int32)).cuda()
-    tok = torch.full((B, T), -7, dtype=torch.int32, device="cuda")
-    par = torch.full((B, T), -7, dtype=torch.int32, device="cuda")
-    nn = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    tok, par, nn = _outs(B, T)
     cfg = hta.make_config(batch=B, n_q_heads=8, n_kv_heads=2, head_dim=128, tree_nodes=T, kv_capacity=64)
+    params = hta.make_tree_params(k, m, keep_first, keep)
     with hta.hta_create(cfg) as h:
-        hta.hta_build_tree(h, lg, hist, hl, hta.make_tree_params(k, m, keep_first, keep), tok, par, nn)
+        if indexed:
+            with hta.hta_ngram_index_create(B, case.history.shape[1], m) as idx:
+                hta.hta_build_tree_indexed(h, idx, lg, hist, hl, params, tok, par, nn)
+                torch.cuda.synchronize()
+        else:
+            hta.hta_build_tree(h, lg, hist, hl, params, tok, par, nn)
         status = hta.hta_get_status(h)
     return tok.cpu().numpy(), par.cpu().numpy(), nn.cpu().numpy(), status
 
 
 def _check(case, k, m, keep_first, keep, T):
-    say(f"hta_build_tree B={case.B} V={case.V} k={k} m={m} T={T} lens={list(case.history_len)[:4]}")
-    tok, par, nn, status = _run(case, k, m, keep_first, keep, T)
-    assert status == 0
     rt, rp, rn = oracle.build_trees(case.history, case.history_len, case.logits_f64(), k, m, keep_first, keep, T)
-    assert np.array_equal(nn, rn)
-    assert np.array_equal(tok, rt)
-    assert np.array_equal(par, rp)
+    for indexed in (False, True):
+        name = "hta_build_tree_indexed" if indexed else "hta_build_tree"
+        say(f"{name} B={case.B} V={case.V} k={k} m={m} T={T} lens={list(case.history_len)[:4]}")
+        tok, par, nn, status = _run(case, k, m, keep_first, keep, T, indexed=indexed)
+        assert status == 0
+        assert np.array_equal(nn, rn), name
+        assert np.array_equal(tok, rt), name
+        assert np.array_equal(par, rp), name
     return rn
 
 
@@ -83,10 +104,12 @@ def test_odd_vocab_and_no_matches():
     _check(case, 5, 3, 4, [4, 3, 2, 1, 1], 16)
 
 
-def test_bad_history_len_gives_empty_tree_and_status():
+@pytest.mark.parametrize("indexed", [False, True])
+@pytest.mark.parametrize("bad", [101, -1])
+def test_bad_history_len_gives_empty_tree_and_status(indexed, bad):
     case = make_tree_case(B=2, V=200, cap=100, history_len=[100, 50], alphabet=5, seed=2)
-    say("hta_build_tree bad history_len")
-    tok, par, nn, status = _run(case, 3, 2, 2, [2, 2, 2], 8, hist_len=[100, 101])
+    say(f"build_tree bad history_len {bad} indexed={indexed}")
+    tok, par, nn, status = _run(case, 3, 2, 2, [2, 2, 2], 8, hist_len=[100, bad], indexed=indexed)
     assert status == hta.HTA_STATUS_BAD_PREFIX
     assert nn[1] == 0 and np.all(tok[1] == -1) and par[1, 0] == -1 and np.all(par[1, 1:] == 0)
     rt, rp, rn = oracle.build_trees(case.history[:1], case.history_len[:1], case.logits_f64()[:1], 3, 2, 2,
@@ -108,3 +131,156 @@ def test_signed_zero_ties(dtype, V):
         case.logits = f32_to_bf16_bits(case.logits)
         case.dtype = "bf16"
     _check(case, 8, 2, 6, [4, 3, 2, 2, 1, 1, 1, 1], 64)
+
+
+# ---------------------------------------------------------------------------
+# The n-gram index across calls: the tokens only grow (a decoding loop), are
+# cut back, or a batch slot starts a new sequence after a reset.
+# ---------------------------------------------------------------------------
+
+class _Session:
+    """One handle and one index over a fixed history buffer; each call checks
+    the indexed build against the oracle on the lengths given."""
+
+    def __init__(self, case, k, m, keep_first, keep, T):
+        self.case, self.k, self.m, self.kf, self.keep, self.T = case, k, m, keep_first, keep, T
+        B, cap = case.history.shape
+        self.h = hta.hta_create(hta.make_config(batch=B, n_q_heads=8, n_kv_heads=2, head_dim=128, tree_nodes=T,
+                                                kv_capacity=64))
+        self.idx = hta.hta_ngram_index_create(B, cap, m)
+        self.hist = torch.from_numpy(case.history).cuda()
+        self.params = hta.make_tree_params(k, m, keep_first, keep)
+
+    def close(self):
+        hta.hta_ngram_index_destroy(self.idx)
+        hta.hta_destroy(self.h)
+
+    def step(self, lens, logits=None):
+        case = self.case
+        lg_np = case.logits if logits is None else logits
+        lg = (torch.from_numpy(np.ascontiguousarray(lg_np).view(np.int16)).view(torch.bfloat16).cuda()
+              if case.dtype == "bf16" else torch.from_numpy(np.ascontiguousarray(lg_np)).cuda())
+        hl = torch.tensor(np.asarray(lens, dtype=np.int32)).cuda()
+        tok, par, nn = _outs(case.B, self.T)
+        hta.hta_build_tree_indexed(self.h, self.idx, lg, self.hist, hl, self.params, tok, par, nn)
+        assert hta.hta_get_status(self.h) == 0
+        lf = (case.logits_f64() if logits is None else
+              (bf16_bits_to_f64(lg_np) if case.dtype == "bf16" else lg_np.astype(np.float64)))
+        rt, rp, rn = oracle.build_trees(case.history, np.asarray(lens), lf, self.k, self.m, self.kf, self.keep,
+                                        self.T)
+        assert np.array_equal(nn.cpu().numpy(), rn)
+        assert np.array_equal(tok.cpu().numpy(), rt)
+        assert np.array_equal(par.cpu().numpy(), rp)
+        return rn
+
+
+def bf16_bits_to_f64(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_index_follows_a_growing_history(m):
+    # a decoding loop: each step appends 1..8 accepted tokens; new logits every step
+    B, cap, V = 3, 6000, 700
+    case = make_tree_case(B=B, V=V, cap=cap, history_len=[cap] * B, alphabet=7, seed=60 + m)
+    rng = np.random.default_rng(m)
+    lens = np.array([0, 2500, 5900])
+    ss = _Session(case, 6, m, 5, [5, 4, 3, 2, 2, 1], 48)
+    try:
+        for it in range(10):
+            say(f"index growing m={m} step {it} lens={list(lens)}")
+            lg = make_tree_case(B=B, V=V, cap=1, history_len=[1] * B, alphabet=7, seed=1000 + it).logits
+            ss.step(lens, lg)
+            lens = np.minimum(cap, lens + rng.integers(1, 9, size=B))
+    finally:
+        ss.close()
+
+
+def test_index_cut_back_rebuilds_and_reset_starts_over():
+    B, cap, V = 2, 5000, 400
+    case = make_tree_case(B=B, V=V, cap=cap, history_len=[cap] * B, alphabet=5, seed=77)
+    ss = _Session(case, 5, 3, 4, [4, 3, 2, 2, 1], 40)
+    try:
+        say("index cut back: lens 4000/4500 -> 1200/4500 -> 1300/4510")
+        ss.step([4000, 4500])
+        ss.step([1200, 4500])  # sequence 0 cut back: its part is rebuilt from position 0
+        ss.step([1300, 4510])
+        say("index reset: sequence 1 gets new tokens")
+        new = np.random.default_rng(5).integers(0, 5, size=cap).astype(np.int32)
+        case.history[1] = new
+        ss.hist[1].copy_(torch.from_numpy(new))
+        hta.hta_ngram_index_reset(ss.idx, 1)
+        ss.step([1310, 3000])
+        hta.hta_ngram_index_reset(ss.idx, -1)
+        ss.step([2000, 2000])
+    finally:
+        ss.close()
+
+
+@pytest.mark.parametrize("m", [1, 2, 8])
+def test_index_one_repeated_token(m):
+    # every gram is the same: all inserts meet in one slot
+    case = make_tree_case(B=2, V=300, cap=20000, history_len=[20000, 7], alphabet=1, seed=9)
+    _check(case, 4, m, 8, [8, 4, 2, 1], 32)
+
+
+def test_index_argument_errors():
+    case = make_tree_case(B=2, V=300, cap=100, history_len=[100, 50], alphabet=5, seed=1)
+    lg = _logits(case)
+    hist = torch.from_numpy(case.history).cuda()
+    hl = torch.from_numpy(case.history_len).cuda()
+    tok, par, nn = _outs(2, 16)
+    cfg = hta.make_config(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, tree_nodes=16, kv_capacity=64)
+    say("index argument errors")
+    with hta.hta_create(cfg) as h, hta.hta_ngram_index_create(2, 100, 3) as idx, \
+            hta.hta_ngram_index_create(1, 100, 3) as idx1:
+        with pytest.raises(RuntimeError, match="invalid argument"):  # m differs from the index's
+            hta.hta_build_tree_indexed(h, idx, lg, hist, hl, hta.make_tree_params(2, 2, 1, [1, 1]), tok, par, nn)
+        lib = hta.load_library()
+        code = lib.hta_build_tree_indexed(ctypes.c_void_p(h.ptr), ctypes.c_void_p(idx1.ptr),
+                                          ctypes.c_void_p(lg.data_ptr()), 300, hta.HTA_BF16,
+                                          ctypes.c_void_p(hist.data_ptr()), ctypes.c_void_p(hl.data_ptr()),
+                                          ctypes.byref(hta.make_tree_params(2, 3, 1, [1, 1])),
+                                          ctypes.c_void_p(tok.data_ptr()), ctypes.c_void_p(par.data_ptr()),
+                                          ctypes.c_void_p(nn.data_ptr()), None)
+        assert code == hta.HTA_ERR_INVALID_ARG  # batch differs from the handle's
+        assert lib.hta_ngram_index_reset(ctypes.c_void_p(idx.ptr), 2, None) == hta.HTA_ERR_INVALID_ARG
+        assert lib.hta_ngram_index_reset(ctypes.c_void_p(idx.ptr), -2, None) == hta.HTA_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert hta.hta_get_status(h) == 0
+
+
+def test_index_in_a_graph_replays_like_eager_calls():
+    # reset + indexed build captured once; replays with eager calls at other
+    # lengths in between must give the oracle's tree every time
+    B, cap, V, T = 2, 4000, 600, 32
+    case = make_tree_case(B=B, V=V, cap=cap, history_len=[3000, 3500], alphabet=6, seed=91)
+    k, m, kf, keep = 5, 3, 4, [4, 3, 2, 2, 1]
+    ss = _Session(case, k, m, kf, keep, T)
+    try:
+        lg = _logits(case)
+        hl = torch.from_numpy(case.history_len).cuda()
+        tok, par, nn = _outs(B, T)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            hta.hta_ngram_index_reset(ss.idx, -1, s)
+            hta.hta_build_tree_indexed(ss.h, ss.idx, lg, ss.hist, hl, ss.params, tok, par, nn, s)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            hta.hta_ngram_index_reset(ss.idx, -1, cs)
+            hta.hta_build_tree_indexed(ss.h, ss.idx, lg, ss.hist, hl, ss.params, tok, par, nn, cs)
+        rt, rp, rn = oracle.build_trees(case.history, case.history_len, case.logits_f64(), k, m, kf, keep, T)
+        for rep in range(3):
+            say(f"index graph replay {rep}")
+            tok.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(nn.cpu().numpy(), rn)
+            assert np.array_equal(tok.cpu().numpy(), rt)
+            assert np.array_equal(par.cpu().numpy(), rp)
+            ss.step([1000 + 500 * rep, 3900 - 100 * rep])  # eager calls move the index elsewhere
+        assert hta.hta_get_status(ss.h) == 0
+    finally:
+        ss.close()
