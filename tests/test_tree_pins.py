@@ -143,3 +143,38 @@ def test_planted_mistakes_fail_the_bigram_example(monkeypatch):
     monkeypatch.setattr(tree_oracle, "most_recent_match",
                         lambda s, gr, before: real(s, gr, len(s)) if gr == s[len(s) - len(gr):] else real(s, gr, before))
     assert list(tree_oracle.build_tree(*args)[0]) != list(good[0])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_latest_gram_index_answers_the_scan_queries(seed):
+    """The reading behind hta_build_tree_indexed: a map from each distinct m-gram
+    of the history alone to the latest position where it ends, filled as the
+    history grows, gives exactly the oracle's most recent earlier match for
+    query 1 (the m tokens ending with x1, searched before x1) and for every
+    query 2 (m-1 tokens ending with x1, then a guess other than x1) over the
+    sequence history + [x1]."""
+    rng = np.random.default_rng(500 + seed)
+    alphabet = int(rng.integers(1, 6))
+    L = int(rng.integers(0, 300))
+    hist = [int(t) for t in rng.integers(0, alphabet, size=L)]
+    for m in range(1, 9):
+        index = {}
+        covered = 0
+        for cut in sorted(set([int(c) for c in rng.integers(0, L + 1, size=3)] + [L])):
+            for e in range(max(covered, m - 1), cut):  # grams ending at the new positions
+                index[tuple(hist[e - m + 1:e + 1])] = e
+            covered = cut
+            h = hist[:cut]
+            for x1 in range(alphabet + 1):
+                seq = h + [x1]
+                n = len(seq)
+                if m <= n:
+                    want = tree_oracle.most_recent_match(seq, seq[n - m:], n - 1)
+                    got = index.get(tuple(seq[n - m:]), -1)
+                    assert got == want, (m, cut, x1)
+                for g in range(alphabet + 1):
+                    if g == x1 or m - 1 > n:
+                        continue
+                    gram = (seq[n - (m - 1):] if m > 1 else []) + [g]
+                    want = tree_oracle.most_recent_match(seq, gram, n)
+                    assert index.get(tuple(gram), -1) == want, (m, cut, x1, g)
