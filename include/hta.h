@@ -242,10 +242,11 @@ HTA_API int hta_build_tree(hta_handle_t h, const void* logits, int32_t vocab, in
  * largest end position at which it occurs, where n = the history length it
  * has been brought up to (kept on the device). Open addressing with linear
  * probing over 2^s slots, 2^s >= 2 * history_cap; a slot holds the end
- * position of the gram's first inserted occurrence (its key, compared token
- * by token against the history, so results never depend on hash collisions)
- * and the largest end position seen. Device memory: B * 2^s * 8 bytes + 8 B
- * bytes, allocated on the current HIP device. */
+ * position of the gram's first inserted occurrence (the key: inserts compare
+ * grams token by token through the history, so results never depend on hash
+ * collisions), the largest end position seen and a copy of the gram's tokens
+ * (what lookups compare). Device memory: B * 2^s * 32 bytes (64 for m >= 7)
+ * + 4 B bytes, allocated on the current HIP device. */
 typedef struct hta_ngram_index_s* hta_ngram_index_t;
 
 /* Creates an empty index for batch sequences of history_cap tokens and grams

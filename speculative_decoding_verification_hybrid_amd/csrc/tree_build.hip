@@ -177,7 +177,7 @@ __device__ __forceinline__ bool gram_ends_at(const int* hist, int r, int m, cons
     if (t < m) eq &= hist[r - m + 1 + t] == w[t];
   return eq;
 }
-// Slot layout, kSlotInts(m) ints: [0] end position of the key occurrence
+// Slot layout, slot_ints(m) ints: [0] end position of the key occurrence
 // (-1: empty), [1] largest end position, [2 .. 2+m) the key's tokens.
 __host__ __device__ constexpr int slot_ints(int m) { return m + 2 <= 8 ? 8 : 16; }
 
