@@ -105,6 +105,14 @@ __device__ __forceinline__ void halve(float* x, bool h) {
   }
 }
 
+// s_waitcnt immediate: wait until at most N vector-memory loads of this wave
+// are in flight (the other counters left alone).
+template <int N>
+constexpr int vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8);
+}
+
 // Lanes of one token's row: CL = D/8 lanes of 8 dims each, so one 16-byte load
 // of the wave covers TPL = 64/CL consecutive tokens and a unit is U = UNIT/TPL
 // loads. Lane (grp, c) = (lane / CL, lane % CL).
@@ -173,11 +181,15 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       __syncthreads();
     }
 
-    // this group's query rows of the KV head, dims 8c..8c+7 (rows past M are zero)
+    // this group's query rows of the KV head, dims 8c..8c+7 (rows past M are
+    // zero; their loads read row M-1, so that every load is issued on every
+    // path and the compiler's count of loads in flight stays exact)
     u32x4 qr[MR];
 #pragma unroll
-    for (int r = 0; r < MR; ++r)
-      qr[r] = r0 + r < a.M ? *(const u32x4*)(qp + (size_t)(r0 + r) * D + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < MR; ++r) {
+      const u32x4 v = *(const u32x4*)(qp + (size_t)min(r0 + r, a.M - 1) * D + 8 * c);
+      qr[r] = r0 + r < a.M ? v : u32x4{0u, 0u, 0u, 0u};
+    }
 
     // ancestor word of the tree node behind each of this lane's rows
     unsigned long long vis_row[NV];
@@ -202,7 +214,12 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
     const int nun = nu > wv ? (nu - wv + NWAVE - 1) / NWAVE : 0;
     auto unit_of = [&](int i) { return wv + NWAVE * i; };  // piece unit of this wave's i-th unit
 
-    // Loads of one unit's K (or V) rows; tokens past the end repeat the last valid row.
+    // Loads of one unit's K (or V) rows; tokens past the end repeat the last
+    // valid row. Branch-free, so that the loads write straight into the
+    // registers the next unit reads: with a branch (or a conditional load) the
+    // compiler merged the paths' results with register copies at the loop's
+    // back edge, and those copies waited for every load in flight, so no load
+    // ever overlapped the next unit.
     auto load_rows = [&](int pu, const unsigned short* base_tree, const unsigned short* base_cache, u32x4* dst) {
       const int ti = tile0 + (pu >> 1);
       const bool tree = ti >= n_prefix;
@@ -210,27 +227,29 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       const int nvalid = tree ? a.T : min(NK, L - ti * NK);  // >= 1 for every tile that exists
       const char* sb = reinterpret_cast<const char*>(src);
       const int t0 = (pu & 1) * UNIT;
-      if (t0 + UNIT <= nvalid) {  // the whole unit is valid: one address, constant offsets
-        const unsigned off = (unsigned)((t0 + grp) * D + 8 * c) * 2u;
 #pragma unroll
-        for (int u = 0; u < U; ++u) dst[u] = *(const u32x4*)(sb + off + u * TPL * D * 2);
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const unsigned tk = (unsigned)min(t0 + TPL * u + grp, nvalid - 1);
-          dst[u] = *(const u32x4*)(sb + (tk * D + 8u * c) * 2u);
-        }
+      for (int u = 0; u < U; ++u) {
+        const unsigned tk = (unsigned)min(t0 + TPL * u + grp, nvalid - 1);
+        dst[u] = *(const u32x4*)(sb + (tk * D + 8u * c) * 2u);
       }
     };
 
     // K and V of one unit live in registers; the next unit's K is requested as
-    // soon as the scores are formed, its V as soon as P*V is done.
+    // soon as the scores are formed, its V as soon as P*V is done (the last
+    // unit requests itself again, which keeps the loop free of branches around
+    // the loads).
     u32x4 kr[U], vr[U];
     if (nun > 0) {
       load_rows(unit_of(0), ktg, kg, kr);
       load_rows(unit_of(0), vtg, vg, vr);
     }
+    // In flight at the top of unit i: K(i), then V(i) (U loads each, in that
+    // order); K(i+1) goes out after the scores, V(i+1) after P*V. So each use
+    // waits until at most U loads are left (explicit, because the compiler's
+    // own count at the loop head is a full drain).
     for (int i = 0; i < nun; ++i) {
+      __builtin_amdgcn_s_waitcnt(vm_wait<U>());  // K(i) has landed; V(i) may still be in flight
+      __builtin_amdgcn_sched_barrier(0);
       const int pu = unit_of(i);
       const int ti = tile0 + (pu >> 1);
       const bool tree = ti >= n_prefix;
@@ -244,7 +263,7 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       // keep the scheduler from hoisting the next loads above their registers' last use
       // (that would need a second buffer and halve the waves per SIMD)
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < nun) load_rows(unit_of(i + 1), ktg, kg, kr);
+      load_rows(unit_of(min(i + 1, nun - 1)), ktg, kg, kr);
       // (at D = 64 the 8 lanes of a token start at the second stage, with
       // the same 4 * MR values left as after the first stage at D = 128)
       if constexpr (CL == 16) halve<kRor8, 4 * MR>(xs, (c >> 3) & 1);
@@ -299,6 +318,8 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
       // executes one wave's accesses in order; the fence keeps the compiler's)
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(vm_wait<U>());  // V(i) has landed; K(i+1) may still be in flight
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int pr = 0; pr < U / 2; ++pr) {
         // P of slots 2pr, 2pr+1 for every row, as bf16x2
@@ -328,7 +349,7 @@ __global__ void __launch_bounds__(256) prefix_dot_kernel(DotArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < nun) load_rows(unit_of(i + 1), vtg, vg, vr);
+      load_rows(unit_of(min(i + 1, nun - 1)), vtg, vg, vr);
       // the next unit's P writes come after these reads
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
