@@ -284,3 +284,36 @@ def test_index_in_a_graph_replays_like_eager_calls():
         assert hta.hta_get_status(ss.h) == 0
     finally:
         ss.close()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_index_random_sessions(seed):
+    # random m, k and kept lengths; per step each sequence grows by 0..12 tokens,
+    # is sometimes cut back, and a slot is sometimes reset with new tokens
+    rng = np.random.default_rng(900 + seed)
+    B, cap, V, T = 3, 3000, 500, 48
+    m = int(rng.integers(1, 9))
+    k = int(rng.integers(0, 9))
+    keep = [int(x) for x in rng.integers(0, 6, size=k)]
+    case = make_tree_case(B=B, V=V, cap=cap, history_len=[cap] * B, alphabet=int(rng.integers(2, 9)),
+                          seed=950 + seed)
+    ss = _Session(case, k, m, int(rng.integers(0, 8)), keep, T)
+    try:
+        lens = rng.integers(0, cap // 2, size=B)
+        for it in range(12):
+            say(f"index random session seed={seed} m={m} k={k} step {it} lens={list(lens)}")
+            lg = make_tree_case(B=B, V=V, cap=1, history_len=[1] * B, alphabet=4, seed=2000 + 31 * seed + it).logits
+            ss.step(lens, lg)
+            lens = np.minimum(cap, lens + rng.integers(0, 13, size=B))
+            if rng.random() < 0.25:  # cut one sequence back
+                b = int(rng.integers(0, B))
+                lens[b] = int(rng.integers(0, lens[b] + 1))
+            if rng.random() < 0.2:  # a new sequence in one slot
+                b = int(rng.integers(0, B))
+                new = rng.integers(0, 5, size=cap).astype(np.int32)
+                case.history[b] = new
+                ss.hist[b].copy_(torch.from_numpy(new))
+                hta.hta_ngram_index_reset(ss.idx, b)
+                lens[b] = int(rng.integers(0, cap))
+    finally:
+        ss.close()
